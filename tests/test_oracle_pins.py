@@ -1,0 +1,403 @@
+"""Pins for the CPU oracle: closed forms, printed values, invariants, brute force.
+
+Each test pins a part of the oracle to something other than itself, so that a
+dropped term, wrong sign, wrong index or transposed operand fails somewhere.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import special, stats
+
+import oracle
+from oracle import ops, rng
+from oracle.model import Config, CONFIGS, forward, backward, init_params, loss_and_grads, tensor_specs
+from transformer_lm_pretraining_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- architecture
+
+def test_param_count_matches_page():
+    g = golden("pds_recipe.json")
+    cfg = CONFIGS["gpt2_124m"]
+    assert (cfg.L, cfg.H, cfg.C, cfg.Tmax, cfg.V, cfg.Vp) == (
+        g["n_layer"], g["n_head"], g["n_embd"], g["context"], g["vocab_real"], g["vocab_padded"])
+    assert oracle.n_params(cfg, padded=False) == g["n_params"]
+    assert len(tensor_specs(cfg)) == g["n_param_tensors"]
+    assert cfg.Vp % g["padded_multiple"] == 0
+    assert oracle.n_params(cfg, padded=True) == g["n_params"] + (cfg.Vp - cfg.V) * cfg.C == 124475904
+
+
+def test_param_count_closed_form_other_configs():
+    def closed(cfg):
+        return cfg.V * cfg.C + cfg.Tmax * cfg.C + cfg.L * (12 * cfg.C ** 2 + 13 * cfg.C) + 2 * cfg.C
+    for name in ("tiny", "wide", "micro", "gpt2_124m"):
+        cfg = CONFIGS[name]
+        assert oracle.n_params(cfg, padded=False) == closed(cfg)
+        assert len(tensor_specs(cfg)) == 12 * cfg.L + 4
+    assert oracle.n_params(CONFIGS["tiny"], padded=False) == 6837888
+    assert oracle.n_params(CONFIGS["wide"], padded=False) == 467857920
+
+
+def test_recipe_constants_match_page():
+    g = golden("pds_recipe.json")
+    assert g["seqs_per_card"] * g["context"] * g["accum_steps"] * g["cards"] == g["tokens_per_step"]
+    assert g["tokens_per_step"] * g["total_steps"] == g["total_tokens"]
+    assert oracle.optim.MAX_LR == g["max_lr"] and oracle.optim.WARMUP == g["warmup_steps"]
+    assert oracle.optim.TOTAL_STEPS == g["total_steps"]
+
+
+# ---------------------------------------------------------------- RNG / init
+
+def test_splitmix64_reference_vector():
+    # Published reference outputs of SplitMix64 (Vigna's splitmix64.c) for seed 1234567.
+    want = [6457827717110365317, 3203168211198807973, 9817491932198370423,
+            4593380528125082431, 16408922859458223821]
+    got = rng.splitmix64(1234567, np.arange(5, dtype=np.uint64))
+    assert [int(x) for x in got] == want
+
+
+def test_box_muller_is_standard_normal():
+    z = rng.tensor_normal(1337, 3, 200000, 1.0).astype(np.float64)
+    assert abs(z.mean()) < 0.01 and abs(z.std() - 1.0) < 0.01
+    assert stats.kstest(z, "norm").pvalue > 1e-3
+    # distinct tensors draw distinct numbers
+    z2 = rng.tensor_normal(1337, 4, 1000, 1.0)
+    assert not np.allclose(z[:1000], z2)
+
+
+def test_init_statistics_and_structure():
+    cfg = CONFIGS["tiny"]
+    P = init_params(cfg, 1337)
+    wte = P["wte"]
+    assert np.all(wte[cfg.V:] == 0)
+    assert abs(wte[:cfg.V].std() / 0.02 - 1) < 0.005
+    resid = 0.02 / math.sqrt(2 * cfg.L)
+    cp = np.concatenate([P[f"h.{l}.attn.c_proj.weight"].ravel() for l in range(cfg.L)]
+                        + [P[f"h.{l}.mlp.c_proj.weight"].ravel() for l in range(cfg.L)])
+    assert abs(cp.std() / resid - 1) < 0.01
+    assert np.all(P["h.0.attn.c_attn.bias"] == 0) and np.all(P["h.1.ln_2.weight"] == 1)
+    assert np.all(P["ln_f.bias"] == 0)
+    # flatten / unflatten round trip and the decayed segment comes first
+    flat = oracle.flatten(cfg, P)
+    back = oracle.unflatten(cfg, flat)
+    for k in P:
+        assert np.array_equal(back[k], P[k])
+    lay = oracle.layout(cfg)
+    n_decay = sum(int(np.prod(s)) for _, s, d in tensor_specs(cfg) if d)
+    assert all((off < n_decay) == dec for off, _, dec in lay.values())
+
+
+# ---------------------------------------------------------------- schedule, clip, AdamW
+
+def test_lr_schedule_closed_forms():
+    assert oracle.lr_at(350) == pytest.approx(3e-4, rel=1e-12)
+    assert oracle.lr_at(700) == pytest.approx(6e-4, rel=1e-12)
+    assert oracle.lr_at((700 + 18865) / 2) == pytest.approx(3e-4, rel=1e-12)
+    assert oracle.lr_at(18865) == pytest.approx(0.0, abs=1e-18)
+    assert oracle.lr_at(1) == pytest.approx(6e-4 / 700)
+
+
+def test_adamw_constant_gradient_from_zero_state():
+    rs = np.random.default_rng(0)
+    p = rs.standard_normal(1000).astype(np.float32) * 0.02
+    g = rs.standard_normal(1000).astype(np.float32) * 1e-3  # norm < 1: no clipping
+    mask = np.arange(1000) < 600
+    lr = 3e-4
+    p1, m1, v1, n = oracle.clip_adamw(p, g, np.zeros_like(p), np.zeros_like(p), mask, 1, lr, dtype=np.float64)
+    # mhat = g, vhat = g^2 exactly at t = 1
+    want = p.astype(np.float64) - lr * (g / (np.abs(g.astype(np.float64)) + 1e-8) + np.where(mask, 0.1, 0) * p)
+    np.testing.assert_allclose(p1, want, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(m1, 0.1 * g.astype(np.float64), rtol=1e-12)
+    np.testing.assert_allclose(v1, 0.05 * g.astype(np.float64) ** 2, rtol=1e-12)
+
+
+def test_adamw_zero_gradient_is_pure_decay():
+    p = np.linspace(-1, 1, 64).astype(np.float64)
+    mask = np.arange(64) < 32
+    p1, m1, v1, n = oracle.clip_adamw(p, np.zeros(64), np.zeros(64), np.zeros(64), mask, 5, 1e-3,
+                                      dtype=np.float64)
+    np.testing.assert_allclose(p1[:32], p[:32] * (1 - 1e-3 * 0.1), rtol=1e-15)
+    np.testing.assert_array_equal(p1[32:], p[32:])
+    assert n == 0.0
+
+
+def test_clip_scales_to_unit_norm():
+    rs = np.random.default_rng(1)
+    g = rs.standard_normal(5000) * 3.0
+    n = oracle.global_norm([g])
+    assert n == pytest.approx(np.linalg.norm(g), rel=1e-12)
+    # with beta1 = 0 the new m equals the clipped gradient
+    _, m, _, _ = oracle.clip_adamw(np.zeros(5000), g, np.zeros(5000), np.zeros(5000), np.zeros(5000, bool),
+                                   1, 0.0, beta1=0.0, dtype=np.float64)
+    assert np.linalg.norm(m) == pytest.approx(1.0, rel=1e-12)
+    # below the threshold nothing is scaled
+    small = g / n * 0.5
+    _, m, _, _ = oracle.clip_adamw(np.zeros(5000), small, np.zeros(5000), np.zeros(5000), np.zeros(5000, bool),
+                                   1, 0.0, beta1=0.0, dtype=np.float64)
+    np.testing.assert_allclose(m, small, rtol=1e-15)
+
+
+# ---------------------------------------------------------------- primitive ops
+
+def test_layernorm_special_cases():
+    C = 16
+    w = np.linspace(0.5, 2, C)
+    b = np.linspace(-1, 1, C)
+    y, mean, rstd = ops.layernorm_fwd(np.full((3, C), 2.5), w, b)
+    np.testing.assert_allclose(y, np.broadcast_to(b, (3, C)), atol=1e-12)
+    x = np.random.default_rng(0).standard_normal((5, C))
+    y, mean, rstd = ops.layernorm_fwd(x, np.ones(C), np.zeros(C), eps=0.0)
+    np.testing.assert_allclose(y.mean(-1), 0, atol=1e-12)
+    np.testing.assert_allclose(y.var(-1), 1, rtol=1e-12)
+    np.testing.assert_allclose(1 / rstd ** 2, x.var(-1), rtol=1e-12)
+
+
+def test_layernorm_backward_rows_sum_to_zero_and_fd():
+    rs = np.random.default_rng(2)
+    x = rs.standard_normal((4, 12))
+    w = rs.standard_normal(12)
+    b = rs.standard_normal(12)
+    dy = rs.standard_normal((4, 12))
+    _, mean, rstd = ops.layernorm_fwd(x, w, b)
+    dx, dw, db = ops.layernorm_bwd(dy, x, w, mean, rstd)
+    np.testing.assert_allclose(dx.sum(-1), 0, atol=1e-12)
+    f = lambda xx, ww, bb: float((ops.layernorm_fwd(xx, ww, bb)[0] * dy).sum())
+    h = 1e-6
+    for (i, j) in [(0, 0), (1, 5), (3, 11)]:
+        e = np.zeros_like(x); e[i, j] = h
+        assert (f(x + e, w, b) - f(x - e, w, b)) / (2 * h) == pytest.approx(dx[i, j], rel=1e-6, abs=1e-9)
+    for j in (0, 7):
+        e = np.zeros_like(w); e[j] = h
+        assert (f(x, w + e, b) - f(x, w - e, b)) / (2 * h) == pytest.approx(dw[j], rel=1e-6)
+        assert (f(x, w, b + e) - f(x, w, b - e)) / (2 * h) == pytest.approx(db[j], rel=1e-6)
+
+
+def test_gelu_special_cases_and_erf_form():
+    assert ops.gelu_fwd(np.array(0.0)) == 0.0
+    assert ops.gelu_grad(np.array(0.0)) == pytest.approx(0.5, abs=1e-15)
+    u = np.linspace(-6, 6, 2001)
+    exact = 0.5 * u * (1 + special.erf(u / math.sqrt(2)))
+    assert np.max(np.abs(ops.gelu_fwd(u) - exact)) < 1e-3  # tanh form approximates the erf form
+    # far tails: identity and zero
+    assert ops.gelu_fwd(np.array(30.0)) == pytest.approx(30.0)
+    assert abs(ops.gelu_fwd(np.array(-30.0))) < 1e-12
+    h = 1e-6
+    fd = (ops.gelu_fwd(u + h) - ops.gelu_fwd(u - h)) / (2 * h)
+    np.testing.assert_allclose(ops.gelu_grad(u), fd, rtol=1e-6, atol=1e-8)
+
+
+def test_attention_single_position_returns_value():
+    rs = np.random.default_rng(3)
+    q, k, v = (rs.standard_normal((2, 3, 1, 8)) for _ in range(3))
+    o, p, lse = ops.attention_fwd(q, k, v)
+    np.testing.assert_allclose(o, v, rtol=1e-15)
+
+
+def test_attention_matches_brute_force_loop():
+    rs = np.random.default_rng(4)
+    B, H, T, d = 1, 2, 5, 4
+    q, k, v = (rs.standard_normal((B, H, T, d)) for _ in range(3))
+    o, p, lse = ops.attention_fwd(q, k, v)
+    for h in range(H):
+        for t in range(T):
+            w = [math.exp(sum(q[0, h, t, i] * k[0, h, s, i] for i in range(d)) / math.sqrt(d))
+                 for s in range(t + 1)]
+            tot = sum(w)
+            for i in range(d):
+                want = sum(w[s] * v[0, h, s, i] for s in range(t + 1)) / tot
+                assert o[0, h, t, i] == pytest.approx(want, rel=1e-12, abs=1e-14)
+            assert lse[0, h, t] == pytest.approx(math.log(tot), rel=1e-12)
+
+
+def test_attention_backward_finite_differences():
+    rs = np.random.default_rng(5)
+    q, k, v = (rs.standard_normal((1, 2, 6, 4)) for _ in range(3))
+    do = rs.standard_normal((1, 2, 6, 4))
+    o, p, _ = ops.attention_fwd(q, k, v)
+    dq, dk, dv = ops.attention_bwd(do, q, k, v, p)
+    f = lambda qq, kk, vv: float((ops.attention_fwd(qq, kk, vv)[0] * do).sum())
+    h = 1e-6
+    for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in [(0, 0, 0, 0), (0, 1, 3, 2), (0, 1, 5, 3)]:
+            e = np.zeros_like(arr); e[idx] = h
+            args = {"q": q, "k": k, "v": v}
+            ap = dict(args); ap[name] = arr + e
+            am = dict(args); am[name] = arr - e
+            fd = (f(ap["q"], ap["k"], ap["v"]) - f(am["q"], am["k"], am["v"])) / (2 * h)
+            assert fd == pytest.approx(grad[idx], rel=1e-6, abs=1e-10)
+
+
+def test_masked_xent_matches_log_softmax_and_ignores_padding():
+    rs = np.random.default_rng(6)
+    V, Vp, R = 61, 64, 7
+    z = rs.standard_normal((R, Vp))
+    z[:, V:] = 1e3  # planted garbage in the padding columns
+    tgt = rs.integers(0, V, R)
+    loss, probs = ops.masked_xent_fwd(z, tgt, V)
+    want = -special.log_softmax(z[:, :V], axis=1)[np.arange(R), tgt]
+    np.testing.assert_allclose(loss, want, rtol=1e-13)
+    dz = ops.masked_xent_bwd(probs, tgt, Vp, 0.25)
+    assert np.all(dz[:, V:] == 0)
+    np.testing.assert_allclose(dz.sum(1), 0, atol=1e-15)
+    # shift invariance of each row's loss
+    loss2, _ = ops.masked_xent_fwd(z + 7.0, tgt, V)
+    np.testing.assert_allclose(loss2, loss, rtol=1e-12)
+
+
+def test_embedding_backward_collisions():
+    tok = np.array([[3, 3, 1], [3, 0, 1]])
+    dx = np.arange(2 * 3 * 2, dtype=np.float64).reshape(2, 3, 2)
+    dwte, dwpe = ops.embedding_bwd(dx, tok, 8, 4)
+    np.testing.assert_array_equal(dwte[3], dx[0, 0] + dx[0, 1] + dx[1, 0])
+    np.testing.assert_array_equal(dwte[1], dx[0, 2] + dx[1, 2])
+    np.testing.assert_array_equal(dwpe[:3], dx.sum(0))
+    assert np.all(dwpe[3] == 0) and np.all(dwte[4:] == 0)
+
+
+# ---------------------------------------------------------------- whole model
+
+def _tiny_batch(cfg, B, T, seed=1337):
+    return synth.micro_batches(1, B, T, cfg.V, seed)[0]
+
+
+def test_zero_embedding_gives_ln_V_exactly():
+    cfg = CONFIGS["tiny"]
+    P = init_params(cfg)
+    P["wte"] = np.zeros_like(P["wte"])
+    tok, tgt = _tiny_batch(cfg, 2, 16)
+    loss, rows, cache = forward(cfg, P, tok, tgt, dtype=np.float64)
+    assert loss == pytest.approx(math.log(50257), abs=1e-12)
+    assert abs(loss - math.log(50304)) > 9e-4
+    G = backward(cfg, P, cache, 1.0 / tok.size)
+    assert np.all(G["wte"][cfg.V:] == 0)
+    probs = cache["probs"]
+    np.testing.assert_allclose(probs, 1.0 / cfg.V, rtol=1e-12)
+
+
+def test_initial_loss_near_ln_V():
+    cfg = CONFIGS["tiny"]
+    P = init_params(cfg)
+    tok, tgt = _tiny_batch(cfg, 4, 64)
+    loss, _, _ = forward(cfg, P, tok, tgt, dtype=np.float32)
+    assert abs(loss - math.log(cfg.V)) < 0.3
+    # With targets independent of the inputs (and never equal to them, so the tied
+    # table's self-logit does not enter), logits are ~Gaussian with variance
+    # C * 0.02^2 (unit-variance LN output against N(0, 0.02) rows), so
+    # E[loss] ~ ln V + C * 0.02^2 / 2.
+    rs = np.random.default_rng(5)
+    tok = rs.integers(0, cfg.V, (4, 64))
+    tgt = (tok + rs.integers(1, cfg.V, (4, 64))) % cfg.V
+    loss, _, _ = forward(cfg, P, tok, tgt, dtype=np.float32)
+    assert loss == pytest.approx(math.log(cfg.V) + cfg.C * 0.02 ** 2 / 2, abs=0.05)
+
+
+def test_causality_bitwise():
+    cfg = CONFIGS["tiny"]
+    P = init_params(cfg)
+    tok, tgt = _tiny_batch(cfg, 2, 32)
+    _, _, c1 = forward(cfg, P, tok, None, dtype=np.float32)
+    tok2 = tok.copy()
+    tok2[:, 20:] = (tok2[:, 20:] + 17) % cfg.V
+    _, _, c2 = forward(cfg, P, tok2, None, dtype=np.float32)
+    for b in range(2):
+        for t in range(20):
+            np.testing.assert_array_equal(c1["logits"][b, t], c2["logits"][b, t])
+    assert not np.array_equal(c1["logits"][:, 20:], c2["logits"][:, 20:])
+
+
+def test_finite_differences_micro_model_fp64():
+    cfg = CONFIGS["micro"]
+    P = {k: v.astype(np.float64) for k, v in init_params(cfg, 7).items()}
+    rs = np.random.default_rng(11)
+    # perturb zero-initialised tensors so every gradient path is exercised
+    for k in P:
+        if k.endswith("bias") or k.startswith("ln_f") or ".ln_" in k:
+            P[k] = P[k] + 0.1 * rs.standard_normal(P[k].shape)
+    P["wte"][cfg.V:] = 0.0
+    tok = rs.integers(0, cfg.V, (2, 8))
+    tgt = rs.integers(0, cfg.V, (2, 8))
+    loss, G, _ = loss_and_grads(cfg, P, tok, tgt, dtype=np.float64)
+
+    def f(PP):
+        return forward(cfg, PP, tok, tgt, dtype=np.float64)[0]
+
+    checked = 0
+    for name, g in G.items():
+        flat_idx = rs.choice(g.size, size=min(10, g.size), replace=False)
+        if name == "wte":  # include rows actually used
+            flat_idx = np.concatenate([flat_idx, [tok[0, 0] * cfg.C + 3, tgt[1, 2] * cfg.C + 5]])
+        for fi in flat_idx:
+            idx = np.unravel_index(fi, g.shape)
+            base = P[name][idx]
+            h = 1e-6 * max(1.0, abs(base))
+            Pp = dict(P); Pp[name] = P[name].copy(); Pp[name][idx] = base + h
+            Pm = dict(P); Pm[name] = P[name].copy(); Pm[name][idx] = base - h
+            fd = (f(Pp) - f(Pm)) / (2 * h)
+            assert fd == pytest.approx(g[idx], rel=1e-5, abs=1e-9), (name, idx)
+            checked += 1
+    assert checked >= 10 * len(G)
+    # padding rows of wte never get gradient
+    assert np.all(G["wte"][cfg.V:] == 0)
+
+
+def test_gradient_invariants_tiny():
+    cfg = CONFIGS["tiny"]
+    P = init_params(cfg)
+    tok, tgt = _tiny_batch(cfg, 2, 32)
+    loss, G, cache = loss_and_grads(cfg, P, tok, tgt, dtype=np.float64)
+    C = cfg.C
+    for l in range(cfg.L):
+        kb = G[f"h.{l}.attn.c_attn.bias"][C:2 * C]
+        qb = G[f"h.{l}.attn.c_attn.bias"][:C]
+        assert np.max(np.abs(kb)) < 1e-12 * max(1.0, np.max(np.abs(qb))) + 1e-15
+    assert np.all(G["wte"][cfg.V:] == 0)
+    assert np.all(G["wpe"][32:] == 0)
+
+
+def test_accumulation_equivalence():
+    cfg = CONFIGS["tiny"]
+    P = init_params(cfg)
+    tok, tgt = _tiny_batch(cfg, 4, 16)
+    _, G_full, _ = loss_and_grads(cfg, P, tok, tgt, dloss=1.0 / tok.size, dtype=np.float64)
+    acc = None
+    for half in (slice(0, 2), slice(2, 4)):
+        _, G, _ = loss_and_grads(cfg, P, tok[half], tgt[half], dloss=1.0 / tok.size, dtype=np.float64)
+        acc = G if acc is None else {k: acc[k] + G[k] for k in acc}
+    for k in G_full:
+        np.testing.assert_allclose(acc[k], G_full[k], rtol=1e-9, atol=1e-14)
+
+
+def test_fp32_vs_fp64_noise_floor():
+    cfg = CONFIGS["tiny"]
+    P = init_params(cfg)
+    tok, tgt = _tiny_batch(cfg, 2, 32)
+    l32, _, _ = forward(cfg, P, tok, tgt, dtype=np.float32)
+    l64, _, _ = forward(cfg, P, tok, tgt, dtype=np.float64)
+    assert abs(l32 - l64) < 1e-5
+
+
+def test_token_stream_structure():
+    V = 50257
+    s = synth.token_stream(200000, V)
+    assert s[0] == V - 1
+    assert s.min() >= 0 and s.max() <= V - 1
+    frac_eot = np.mean(s == V - 1)
+    assert 0.018 < frac_eot < 0.031  # 1/(40+1)
+    body = s[s != V - 1]
+    cdf = synth.zipf_cdf(V - 1)
+    assert np.mean(body == 0) == pytest.approx(cdf[0], abs=0.005)
+    assert cdf[0] == pytest.approx(1 / special.zeta(1.1, 1) / (1 - special.zeta(1.1, V) / special.zeta(1.1, 1)),
+                                   rel=1e-9)
+    b = synth.micro_batches(2, 3, 8, V)
+    np.testing.assert_array_equal(b[0][1][:, :-1], b[0][0][:, 1:])
+    np.testing.assert_array_equal(b[0][1][0, -1], b[0][0][1, 0])
