@@ -1,0 +1,112 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, plans sizes/layout consistently with the oracle, and rejects bad
+arguments.  No GPU compute is called."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.model import CONFIGS
+from transformer_lm_pretraining_amd import lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for h in ("gpt2mi.h", "gpt2mi_kernels.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s+(gpt2k?_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return lib.load()
+
+
+def cfg_of(name, B=2, T=None):
+    c = CONFIGS[name]
+    return lib.make_config(c.L, c.H, c.C, c.V, c.Vp, c.Tmax, B, T or c.Tmax)
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 30
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(lib.EXPORTED)
+
+
+def test_sizes_match_oracle_counts(L):
+    for name, (B, T) in (("gpt2_124m", (19, 1024)), ("tiny", (4, 64)), ("wide", (8, 1024))):
+        c = CONFIGS[name]
+        s = lib.sizes(cfg_of(name, B, T))
+        assert s.n_params == oracle.n_params(c, padded=True)
+        assert s.n_params_real == oracle.n_params(c, padded=False)
+        assert s.n_tensors == 12 * c.L + 4
+        n_decay = sum(int(np.prod(sh)) for _, sh, d in oracle.tensor_specs(c) if d)
+        assert s.n_decay == n_decay
+        assert s.acts_bytes > 0 and s.scratch_bytes > 0
+    s = lib.sizes(cfg_of("gpt2_124m", 19, 1024))
+    assert s.n_params_real == 124439808
+    assert s.n_params == 124475904 and s.n_decay == 124354560
+
+
+def test_tensor_table_matches_oracle_layout(L):
+    for name in ("tiny", "gpt2_124m"):
+        c = CONFIGS[name]
+        lay = oracle.layout(c)
+        table = lib.tensor_table(cfg_of(name))
+        assert [t[0] for t in table] == list(lay.keys())
+        for n, off, rows, cols, dec, toff in table:
+            o_off, shape, o_dec = lay[n]
+            assert off == o_off and dec == o_dec
+            assert rows * cols == int(np.prod(shape))
+            if len(shape) == 2:
+                assert (rows, cols) == shape
+
+
+@pytest.mark.parametrize("field,value", [("C", 100), ("H", 5), ("Vp", 50257), ("T", 2048), ("T", 100),
+                                         ("V", 60000), ("B", 0), ("L", 0)])
+def test_invalid_configs_rejected(L, field, value):
+    cfg = cfg_of("tiny", 4, 64)
+    setattr(cfg, field, value)
+    s = lib.Sizes()
+    assert L.gpt2_sizes(ctypes.byref(cfg), ctypes.byref(s)) == lib.GPT2_E_INVALID
+
+
+def test_init_rejects_bad_buffers_and_missing_gpu(L):
+    cfg = cfg_of("tiny", 4, 64)
+    h = ctypes.c_void_p()
+    bad = lib.Buffers(*([256] * 7 + [0]))  # null scratch
+    assert L.gpt2_init(ctypes.byref(cfg), 1337, None, ctypes.byref(bad), None, ctypes.byref(h)) == lib.GPT2_E_INVALID
+    mis = lib.Buffers(*([256] * 7 + [257]))  # misaligned
+    assert L.gpt2_init(ctypes.byref(cfg), 1337, None, ctypes.byref(mis), None, ctypes.byref(h)) == lib.GPT2_E_INVALID
+    import torch
+    if not torch.cuda.is_available():
+        ok = lib.Buffers(*([256 * (i + 1) for i in range(8)]))
+        # aligned fake pointers: with no gfx950 device the call must refuse, not fall back
+        assert L.gpt2_init(ctypes.byref(cfg), 1337, None, ctypes.byref(ok), None,
+                           ctypes.byref(h)) == lib.GPT2_E_UNSUPPORTED
+
+
+def test_kernel_entry_points_validate_before_launch(L):
+    # null pointers / bad shapes are refused without touching a device
+    assert L.gpt2k_xent(None, None, None, 4, 10, 128, 1.0, 1, None, None) == lib.GPT2_E_INVALID
+    assert L.gpt2k_gemm_nt(256, 256, None, None, 256, 64, 64, 65, None) == lib.GPT2_E_INVALID
+    assert L.gpt2k_attention_fwd(256, 256, 256, 1, 100, 2, 128, None) == lib.GPT2_E_INVALID
+    assert L.gpt2k_attention_fwd(256, 256, 256, 1, 64, 1, 128, None) == lib.GPT2_E_SHAPE
+    assert L.gpt2k_layernorm_fwd(256, 256, 256, 256, 256, 256, 4, 100, None) == lib.GPT2_E_SHAPE
+    out = ctypes.c_int64()
+    assert L.gpt2k_scratch_bytes(1, 19456, 768, 0, ctypes.byref(out)) == 0 and out.value > 0
+    assert L.gpt2k_scratch_bytes(9, 1, 1, 1, ctypes.byref(out)) == lib.GPT2_E_INVALID
+
+
+def test_strerror(L):
+    for s in range(7):
+        assert L.gpt2_strerror(s)

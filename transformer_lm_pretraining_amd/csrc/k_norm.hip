@@ -1,0 +1,237 @@
+// LayerNorm forward / backward (PDS model text around Fig. 1: normalisation
+// before attention and before the feed-forward part; §4 precision paragraph:
+// statistics in fp32).  One wavefront per row: each lane keeps C/64 values in
+// registers, so a row is read once; statistics are wavefront reductions.
+// The backward also adds the row's input gradient into the residual-stream
+// gradient and produces per-block fp32 partial column sums of dy*xhat and dy,
+// which a second small kernel folds into dw, db.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr float LN_EPS = 1e-5f;
+constexpr int ROWS_PER_BLOCK = 4;  // one wave per row, 4 waves per block
+
+// Lane element mapping: element (j*64 + lane)*VEC + v, j < NV, v < VEC.
+template <int VEC>
+struct Vec;
+template <>
+struct Vec<2> {
+    typedef uint32_t T;
+    __device__ static void unpack(T w, float* f) { f[0] = bflo(w); f[1] = bfhi(w); }
+    __device__ static T pack(const float* f) { return pack_bf2(f[0], f[1]); }
+};
+template <>
+struct Vec<4> {
+    typedef u32x2 T;
+    __device__ static void unpack(T w, float* f) { f[0] = bflo(w.x); f[1] = bfhi(w.x); f[2] = bflo(w.y); f[3] = bfhi(w.y); }
+    __device__ static T pack(const float* f) { return T{pack_bf2(f[0], f[1]), pack_bf2(f[2], f[3])}; }
+};
+
+template <int VEC, int NV>
+__global__ __launch_bounds__(256) void ln_fwd_kernel(const uint16_t* __restrict__ x, const float* __restrict__ w,
+                                                     const float* __restrict__ b, uint16_t* __restrict__ y,
+                                                     float* __restrict__ mean_out, float* __restrict__ rstd_out,
+                                                     int64_t rows) {
+    constexpr int C = NV * 64 * VEC;
+    typedef typename Vec<VEC>::T VT;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const VT* xr = (const VT*)(x + row * C);
+    float v[NV][VEC];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) Vec<VEC>::unpack(xr[j * 64 + lane], v[j]);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s += v[j][e];
+    const float mean = wave_sum(s) * (1.0f / C);
+    float q = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            float d = v[j][e] - mean;
+            q += d * d;
+        }
+    const float var = wave_sum(q) * (1.0f / C);
+    const float rstd = 1.0f / sqrtf(var + LN_EPS);
+    VT* yr = (VT*)(y + row * C);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        float o[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            int c = (j * 64 + lane) * VEC + e;
+            o[e] = (v[j][e] - mean) * rstd * w[c] + b[c];
+        }
+        yr[j * 64 + lane] = Vec<VEC>::pack(o);
+    }
+    if (lane == 0) {
+        mean_out[row] = mean;
+        rstd_out[row] = rstd;
+    }
+}
+
+template <int VEC, int NV>
+__global__ __launch_bounds__(256) void ln_bwd_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy,
+                                                     const float* __restrict__ w, const float* __restrict__ mean,
+                                                     const float* __restrict__ rstd, uint16_t* __restrict__ dres,
+                                                     int accumulate, float* __restrict__ partial, int64_t rows) {
+    constexpr int C = NV * 64 * VEC;
+    typedef typename Vec<VEC>::T VT;
+    __shared__ float red[ROWS_PER_BLOCK][2][C];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    float wv[NV][VEC], dw_acc[NV][VEC], db_acc[NV][VEC];
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            wv[j][e] = w[(j * 64 + lane) * VEC + e];
+            dw_acc[j][e] = 0.f;
+            db_acc[j][e] = 0.f;
+        }
+    const int64_t stride = (int64_t)gridDim.x * ROWS_PER_BLOCK;
+    for (int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + wave; row < rows; row += stride) {
+        const VT* xr = (const VT*)(x + row * C);
+        const VT* dyr = (const VT*)(dy + row * C);
+        const float mu = mean[row], rs = rstd[row];
+        float xh[NV][VEC], g[NV][VEC], wdy[NV][VEC];
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            Vec<VEC>::unpack(xr[j * 64 + lane], xh[j]);
+            Vec<VEC>::unpack(dyr[j * 64 + lane], g[j]);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                xh[j][e] = (xh[j][e] - mu) * rs;
+                wdy[j][e] = wv[j][e] * g[j][e];
+                s1 += wdy[j][e];
+                s2 += wdy[j][e] * xh[j][e];
+                dw_acc[j][e] += g[j][e] * xh[j][e];
+                db_acc[j][e] += g[j][e];
+            }
+        }
+        s1 = wave_sum(s1) * (1.0f / C);
+        s2 = wave_sum(s2) * (1.0f / C);
+        VT* dr = (VT*)(dres + row * C);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            float o[VEC], prev[VEC];
+            if (accumulate) Vec<VEC>::unpack(dr[j * 64 + lane], prev);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                o[e] = (wdy[j][e] - s1 - xh[j][e] * s2) * rs;
+                if (accumulate) o[e] += prev[e];
+            }
+            dr[j * 64 + lane] = Vec<VEC>::pack(o);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            red[wave][0][(j * 64 + lane) * VEC + e] = dw_acc[j][e];
+            red[wave][1][(j * 64 + lane) * VEC + e] = db_acc[j][e];
+        }
+    __syncthreads();
+    for (int c = threadIdx.x; c < 2 * C; c += blockDim.x) {
+        int k = c / C, cc = c % C;
+        float s = 0.f;
+#pragma unroll
+        for (int r = 0; r < ROWS_PER_BLOCK; ++r) s += red[r][k][cc];
+        partial[(int64_t)blockIdx.x * 2 * C + c] = s;
+    }
+}
+
+// out0[c] += sum_b partial[b][0][c], out1[c] += sum_b partial[b][1][c] (out1 may be null
+// when the partial rows hold a single array: then nparts arrays of width C).
+__global__ void fold_partials_kernel(const float* __restrict__ partial, int nblocks, int C, int arrays,
+                                     float* __restrict__ out0, float* __restrict__ out1) {
+    int c = blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= arrays * C) return;
+    double s = 0.0;
+    for (int b = 0; b < nblocks; ++b) s += partial[(int64_t)b * arrays * C + c];
+    if (c < C)
+        out0[c] += (float)s;
+    else
+        out1[c - C] += (float)s;
+}
+
+int ln_blocks(int64_t rows) { return (int)std::min<int64_t>(512, cdiv(rows, ROWS_PER_BLOCK)); }
+
+template <int VEC, int NV>
+hipError_t ln_fwd_t(const uint16_t* x, const float* w, const float* b, uint16_t* y, float* mean, float* rstd,
+                    int64_t rows, hipStream_t s) {
+    hipLaunchKernelGGL((ln_fwd_kernel<VEC, NV>), dim3(cdiv(rows, ROWS_PER_BLOCK)), dim3(256), 0, s, x, w, b, y, mean,
+                       rstd, rows);
+    return hipGetLastError();
+}
+
+template <int VEC, int NV>
+hipError_t ln_bwd_t(const uint16_t* x, const uint16_t* dy, const float* w, const float* mean, const float* rstd,
+                    uint16_t* dres, int accumulate, float* dw, float* db, float* partial, int64_t rows,
+                    hipStream_t s) {
+    constexpr int C = NV * 64 * VEC;
+    int blocks = ln_blocks(rows);
+    hipLaunchKernelGGL((ln_bwd_kernel<VEC, NV>), dim3(blocks), dim3(256), 0, s, x, dy, w, mean, rstd, dres,
+                       accumulate, partial, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fold_partials_kernel, dim3(cdiv(2 * C, 256)), dim3(256), 0, s, partial, blocks, C, 2, dw, db);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+#define LN_CASES(X)  \
+    X(128, 2, 1)     \
+    X(256, 4, 1)     \
+    X(384, 2, 3)     \
+    X(512, 4, 2)     \
+    X(768, 4, 3)     \
+    X(1024, 4, 4)    \
+    X(1536, 4, 6)    \
+    X(2048, 4, 8)    \
+    X(3072, 4, 12)
+
+hipError_t launch_layernorm_fwd(const uint16_t* x, const float* w, const float* b, uint16_t* y, float* mean,
+                                float* rstd, int64_t rows, int C, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    switch (C) {
+#define X(c, vec, nv) \
+    case c: return ln_fwd_t<vec, nv>(x, w, b, y, mean, rstd, rows, s);
+        LN_CASES(X)
+#undef X
+    }
+    return hipErrorInvalidValue;
+}
+
+int64_t layernorm_bwd_partial_elems(int64_t rows, int C) { return (int64_t)ln_blocks(rows) * 2 * C; }
+
+hipError_t launch_layernorm_bwd(const uint16_t* x, const uint16_t* dy, const float* w, const float* mean,
+                                const float* rstd, uint16_t* dres, int accumulate, float* dw, float* db,
+                                float* partial, int64_t rows, int C, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    switch (C) {
+#define X(c, vec, nv) \
+    case c: return ln_bwd_t<vec, nv>(x, dy, w, mean, rstd, dres, accumulate, dw, db, partial, rows, s);
+        LN_CASES(X)
+#undef X
+    }
+    return hipErrorInvalidValue;
+}
+
+bool layernorm_supports(int C) {
+    switch (C) {
+#define X(c, vec, nv) \
+    case c: return true;
+        LN_CASES(X)
+#undef X
+    }
+    return false;
+}

@@ -1,0 +1,191 @@
+// Global-norm clipping + AdamW (PDS §4 optimisation paragraph: AdamW with
+// betas (0.9, 0.95), eps 1e-8, weight decay 0.1 on two-dimensional weights
+// only, clipping to global norm 1.0; §4 precision: fp32 master weights,
+// gradients and optimizer state), plus the seeded init and bf16 shadow
+// maintenance.  All HBM-bound: float4 vectors, grid-stride loops.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int NORM_BLOCKS = 1024;
+constexpr int OPT_THREADS = 256;
+
+// Per-block sum of squares of g (fp32 per thread, fp64 across the block).
+__global__ __launch_bounds__(OPT_THREADS) void sumsq_kernel(const float4* __restrict__ g, int64_t n4,
+                                                            double* __restrict__ partial) {
+    __shared__ double red[OPT_THREADS / 64];
+    float s = 0.f;
+    for (int64_t i = blockIdx.x * (int64_t)OPT_THREADS + threadIdx.x; i < n4; i += (int64_t)gridDim.x * OPT_THREADS) {
+        float4 v = g[i];
+        s += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    double d = wave_sum_d((double)s);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = d;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = 0.0;
+        for (int w = 0; w < OPT_THREADS / 64; ++w) t += red[w];
+        partial[blockIdx.x] = t;
+    }
+}
+
+// norm = sqrt(sum of partials) (fp64); scale = min(1, max_norm / norm).
+__global__ __launch_bounds__(OPT_THREADS) void norm_finalize_kernel(const double* __restrict__ partial, int nparts,
+                                                                    float max_norm, float* __restrict__ scale_out,
+                                                                    float* __restrict__ norm_out) {
+    __shared__ double red[OPT_THREADS / 64];
+    double s = 0.0;
+    for (int i = threadIdx.x; i < nparts; i += OPT_THREADS) s += partial[i];
+    s = wave_sum_d(s);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = 0.0;
+        for (int w = 0; w < OPT_THREADS / 64; ++w) t += red[w];
+        double norm = sqrt(t);
+        double sc = (norm > (double)max_norm) ? (double)max_norm / norm : 1.0;
+        scale_out[0] = (float)sc;
+        if (norm_out) norm_out[0] = (float)norm;
+    }
+}
+
+struct AdamwDev {
+    float lr, beta1, beta2, eps, wd, inv_bc1, inv_bc2;
+};
+
+__device__ __forceinline__ float adam_one(float& p, float g, float& m, float& v, float wd, const AdamwDev& a) {
+    m = a.beta1 * m + (1.0f - a.beta1) * g;
+    v = a.beta2 * v + (1.0f - a.beta2) * g * g;
+    const float mhat = m * a.inv_bc1;
+    const float vhat = v * a.inv_bc2;
+    p = p - a.lr * (mhat / (sqrtf(vhat) + a.eps) + wd * p);
+    return p;
+}
+
+__global__ __launch_bounds__(OPT_THREADS) void adamw_kernel(float4* __restrict__ p, float4* __restrict__ g,
+                                                            float4* __restrict__ m, float4* __restrict__ v,
+                                                            uint2* __restrict__ shadow, int64_t n4,
+                                                            int64_t n_decay4, AdamwDev a,
+                                                            const float* __restrict__ scale_ptr) {
+    const float sc = scale_ptr[0];
+    for (int64_t i = blockIdx.x * (int64_t)OPT_THREADS + threadIdx.x; i < n4; i += (int64_t)gridDim.x * OPT_THREADS) {
+        float4 pp = p[i], gg = g[i], mm = m[i], vv = v[i];
+        const bool dec = i < n_decay4;
+        const float wd = dec ? a.wd : 0.0f;
+        adam_one(pp.x, gg.x * sc, mm.x, vv.x, wd, a);
+        adam_one(pp.y, gg.y * sc, mm.y, vv.y, wd, a);
+        adam_one(pp.z, gg.z * sc, mm.z, vv.z, wd, a);
+        adam_one(pp.w, gg.w * sc, mm.w, vv.w, wd, a);
+        p[i] = pp;
+        m[i] = mm;
+        v[i] = vv;
+        g[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (dec && shadow) shadow[i] = make_uint2(pack_bf2(pp.x, pp.y), pack_bf2(pp.z, pp.w));
+    }
+}
+
+__global__ __launch_bounds__(OPT_THREADS) void cast_bf16_kernel(const float4* __restrict__ src,
+                                                                uint2* __restrict__ dst, int64_t n4) {
+    for (int64_t i = blockIdx.x * (int64_t)OPT_THREADS + threadIdx.x; i < n4; i += (int64_t)gridDim.x * OPT_THREADS) {
+        float4 x = src[i];
+        dst[i] = make_uint2(pack_bf2(x.x, x.y), pack_bf2(x.z, x.w));
+    }
+}
+
+// 64x64 tiles through LDS: dst[c][r] = src[r][c].
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src,
+                                                             uint16_t* __restrict__ dst, int R, int Cc) {
+    __shared__ uint16_t tile[64][65];
+    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+    for (int k = threadIdx.x; k < 64 * 64; k += 256) {
+        int rr = k / 64, cc = k % 64;
+        int r = r0 + rr, c = c0 + cc;
+        tile[rr][cc] = (r < R && c < Cc) ? src[(int64_t)r * Cc + c] : (uint16_t)0;
+    }
+    __syncthreads();
+    for (int k = threadIdx.x; k < 64 * 64; k += 256) {
+        int cc = k / 64, rr = k % 64;
+        int r = r0 + rr, c = c0 + cc;
+        if (r < R && c < Cc) dst[(int64_t)c * R + r] = tile[rr][cc];
+    }
+}
+
+__global__ void fill_f32_kernel(float* __restrict__ dst, float val, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        dst[i] = val;
+}
+
+// SplitMix64 (Steele, Lea & Flood 2014) as a counter-based hash.
+__device__ __forceinline__ uint64_t splitmix_at(uint64_t seed, uint64_t counter) {
+    uint64_t z = seed + (counter + 1ull) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// Box-Muller normal for element e of tensor `tensor`, scaled and rounded to fp32.
+__global__ void init_normal_kernel(float* __restrict__ dst, int64_t n, uint64_t seed, uint64_t tensor_base,
+                                   double stdv, int64_t zero_from) {
+    const double two_pi = 6.283185307179586476925286766559;
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+        if (e >= zero_from) {
+            dst[e] = 0.0f;
+            continue;
+        }
+        const uint64_t x1 = tensor_base + 2ull * (uint64_t)e;
+        const double u1 = ((double)(splitmix_at(seed, x1) >> 11) + 0.5) * 0x1.0p-53;
+        const double u2 = ((double)(splitmix_at(seed, x1 + 1ull) >> 11) + 0.5) * 0x1.0p-53;
+        const double z = sqrt(-2.0 * log(u1)) * cos(two_pi * u2);
+        dst[e] = (float)(stdv * z);
+    }
+}
+
+int grid_for(int64_t n, int cap = 4096) { return (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, 256), cap)); }
+
+}  // namespace
+
+int64_t adamw_partial_elems(int64_t) { return NORM_BLOCKS; }
+
+hipError_t launch_clip_adamw(float* p, float* g, float* m, float* v, uint16_t* shadow, int64_t n, int64_t n_decay,
+                             const AdamwHostArgs& a, float* norm_dev, double* partial, float* scale_dev,
+                             hipStream_t s) {
+    const int64_t n4 = n / 4;
+    hipLaunchKernelGGL(sumsq_kernel, dim3(NORM_BLOCKS), dim3(OPT_THREADS), 0, s, (const float4*)g, n4, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(norm_finalize_kernel, dim3(1), dim3(OPT_THREADS), 0, s, partial, NORM_BLOCKS, a.max_norm,
+                       scale_dev, norm_dev);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    AdamwDev d{a.lr, a.beta1, a.beta2, a.eps, a.wd, a.inv_bc1, a.inv_bc2};
+    hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(n4, 8192)), dim3(OPT_THREADS), 0, s, (float4*)p, (float4*)g,
+                       (float4*)m, (float4*)v, (uint2*)shadow, n4, n_decay / 4, d, (const float*)scale_dev);
+    return hipGetLastError();
+}
+
+hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {
+    hipLaunchKernelGGL(cast_bf16_kernel, dim3(grid_for(n / 4)), dim3(OPT_THREADS), 0, s, (const float4*)src,
+                       (uint2*)dst, n / 4);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int R, int Cc, hipStream_t s) {
+    dim3 grid((unsigned)cdiv(Cc, 64), (unsigned)cdiv(R, 64));
+    hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, src, dst, R, Cc);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* dst, float val, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_for(n)), dim3(256), 0, s, dst, val, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_init_normal(float* dst, int64_t n, uint64_t seed, int tensor, double stdv, int64_t zero_from,
+                              hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(init_normal_kernel, dim3(grid_for(n)), dim3(256), 0, s, dst, n, seed,
+                       (uint64_t)tensor << 40, stdv, zero_from);
+    return hipGetLastError();
+}
