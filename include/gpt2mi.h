@@ -215,24 +215,22 @@ void gpt2_destroy(gpt2_handle* h);
 const char* gpt2_strerror(int status);
 
 /*
- * Kernel timing: while enabled, every launch of kernel class `kclass` (see
- * GPT2_K_* below) issued by this handle is bracketed by HIP events on its
- * stream.  gpt2_prof_read synchronises the stream and returns the summed
- * duration (ms), the launch count and the summed algorithmic work of those
- * launches (FLOP for GEMM/attention classes, bytes for memory-bound classes),
- * then resets the counters.  At most 4096 launches are recorded between reads.
+ * Kernel timing.  gpt2_prof_enable(h, kclass) starts recording: every launch
+ * issued by this handle's gpt2_forward / gpt2_backward / gpt2_clip_adamw /
+ * gpt2_eval_loss whose kernel class equals kclass (-1: every class; 0: stop)
+ * is bracketed by a pair of HIP events on its stream, and the previous
+ * records are dropped.  A class id names exactly one compiled kernel; its
+ * name is gpt2_prof_class_name(kclass) (NULL for an unknown id), ids run
+ * from 1 to 25.  gpt2_prof_read synchronises the stream and sums, over the
+ * recorded launches of class kclass (-1: all), the event-measured duration
+ * (ms), the launch count and the algorithmic work (FLOP for the MFMA kernels
+ * gemm_* and attn_fwd/dkdv/dq, bytes moved for the others).  At most 65,536
+ * launches are recorded after an enable.  Errors: GPT2_E_INVALID, GPT2_E_HIP.
  */
-#define GPT2_K_GEMM_FWD 1       /* forward NT GEMMs (QKV, proj, FC, FC-proj, lm_head) */
-#define GPT2_K_GEMM_DX 2        /* backward input-gradient GEMMs */
-#define GPT2_K_GEMM_DW 3        /* backward weight-gradient GEMMs */
-#define GPT2_K_ATTN_FWD 4
-#define GPT2_K_ATTN_BWD 5
-#define GPT2_K_XENT 6
-#define GPT2_K_LAYERNORM 7
-#define GPT2_K_ADAMW 8
-#define GPT2_K_LMHEAD_FWD 9     /* only the lm_head forward GEMM */
 int gpt2_prof_enable(gpt2_handle* h, int32_t kclass);
-int gpt2_prof_read(gpt2_handle* h, hipStream_t stream, double* total_ms, int64_t* launches, double* work);
+int gpt2_prof_read(gpt2_handle* h, hipStream_t stream, int32_t kclass, double* total_ms, int64_t* launches,
+                   double* work);
+const char* gpt2_prof_class_name(int32_t kclass);
 
 #ifdef __cplusplus
 }

@@ -15,6 +15,7 @@
 #include "../../include/gpt2mi.h"
 #include "../../include/gpt2mi_kernels.h"
 #include "kernels.h"
+#include "prof.h"
 
 namespace {
 
@@ -167,9 +168,11 @@ ScratchPlan plan_scratch(const gpt2_config& c) {
     return s;
 }
 
-constexpr int PROF_MAX = 4096;
+constexpr int PROF_MAX = 65536;
 
 }  // namespace
+
+thread_local ProfSink* g_prof_sink = nullptr;
 
 struct gpt2_handle {
     gpt2_config cfg;
@@ -181,10 +184,29 @@ struct gpt2_handle {
     int last_hip = 0;
     bool grad_ready = false;
     const int32_t* last_tok = nullptr;
-    // kernel timing
+    // kernel timing: class filter (0 off, -1 all), event pairs and records
+    struct Rec {
+        int cls;
+        double work;
+    };
+    struct Sink : ProfSink {
+        gpt2_handle* h = nullptr;
+        bool active = false;
+        void begin(int cls, double work, hipStream_t s) override {
+            active = false;
+            if ((h->prof_class != -1 && h->prof_class != cls) || (int)h->recs.size() >= PROF_MAX) return;
+            const size_t n = h->recs.size();
+            if (hipEventRecord(h->ev0[n], s) != hipSuccess) return;
+            h->recs.push_back({cls, work});
+            active = true;
+        }
+        void end(int, hipStream_t s) override {
+            if (active) hipEventRecord(h->ev1[h->recs.size() - 1], s);
+            active = false;
+        }
+    } sink;
     int prof_class = 0;
-    int prof_n = 0;
-    double prof_work = 0.0;
+    std::vector<Rec> recs;
     std::vector<hipEvent_t> ev0, ev1;
 
     char* A() const { return (char*)bufs.acts; }
@@ -206,22 +228,11 @@ struct gpt2_handle {
 
 namespace {
 
-struct Prof {
-    gpt2_handle* h;
-    hipStream_t s;
-    double work;
-    bool on;
-    Prof(gpt2_handle* h_, int cls, double w, hipStream_t s_, int cls2 = 0) : h(h_), s(s_), work(w) {
-        on = h->prof_class != 0 && (h->prof_class == cls || (cls2 && h->prof_class == cls2)) && h->prof_n < PROF_MAX;
-        if (on) hipEventRecord(h->ev0[h->prof_n], s);
-    }
-    ~Prof() {
-        if (on) {
-            hipEventRecord(h->ev1[h->prof_n], s);
-            h->prof_n++;
-            h->prof_work += work;
-        }
-    }
+// Installs the handle's timing sink for the duration of one API call.
+struct SinkGuard {
+    ProfSink* prev;
+    explicit SinkGuard(gpt2_handle* h) : prev(g_prof_sink) { g_prof_sink = h->prof_class ? &h->sink : nullptr; }
+    ~SinkGuard() { g_prof_sink = prev; }
 };
 
 #define HIPCHK(expr)                          \
@@ -261,62 +272,32 @@ int run_forward(gpt2_handle* h, const int32_t* tok, const int32_t* tgt, float dl
     for (int l = 0; l < c.L; ++l) {
         const LayerActs& la = h->acts.layer[l];
         const int64_t xnext = (l + 1 < c.L) ? h->acts.layer[l + 1].x : h->acts.xfinal;
-        {
-            Prof p(h, GPT2_K_LAYERNORM, 2.0 * BT * C * 2, s);
-            HIPCHK(launch_layernorm_fwd(h->act<uint16_t>(la.x), h->P(h->i_vec(l, 0)), h->P(h->i_vec(l, 1)),
-                                        h->act<uint16_t>(la.ln1), h->act<float>(la.mean1), h->act<float>(la.rstd1), BT,
-                                        C, s));
-        }
-        {
-            Prof p(h, GPT2_K_GEMM_FWD, gemm_flops(BT, 3 * C, C), s);
-            HIPCHK(launch_gemm_nt(h->act<uint16_t>(la.ln1), C, h->W(h->i_mat(l, 0)), C, BT, 3 * C, C,
-                                  h->P(h->i_vec(l, 2)), nullptr, 0, h->act<uint16_t>(la.qkv), 3 * C, s));
-        }
-        {
-            Prof p(h, GPT2_K_ATTN_FWD, attn_flops(c, 2), s);
-            HIPCHK(launch_attention_fwd(h->act<uint16_t>(la.qkv), h->act<uint16_t>(la.att), h->act<float>(la.lse), c.B,
-                                        c.T, c.H, C, s));
-        }
-        {
-            Prof p(h, GPT2_K_GEMM_FWD, gemm_flops(BT, C, C), s);
-            HIPCHK(launch_gemm_nt(h->act<uint16_t>(la.att), C, h->W(h->i_mat(l, 1)), C, BT, C, C, h->P(h->i_vec(l, 3)),
-                                  h->act<uint16_t>(la.x), C, h->act<uint16_t>(la.xmid), C, s));
-        }
-        {
-            Prof p(h, GPT2_K_LAYERNORM, 2.0 * BT * C * 2, s);
-            HIPCHK(launch_layernorm_fwd(h->act<uint16_t>(la.xmid), h->P(h->i_vec(l, 4)), h->P(h->i_vec(l, 5)),
-                                        h->act<uint16_t>(la.ln2), h->act<float>(la.mean2), h->act<float>(la.rstd2), BT,
-                                        C, s));
-        }
-        {
-            Prof p(h, GPT2_K_GEMM_FWD, gemm_flops(BT, 4 * C, C), s);
-            HIPCHK(launch_gemm_nt_gelu(h->act<uint16_t>(la.ln2), C, h->W(h->i_mat(l, 2)), C, BT, 4 * C, C,
-                                       h->P(h->i_vec(l, 6)), h->act<uint16_t>(la.pre), h->act<uint16_t>(la.gel), 4 * C,
-                                       s));
-        }
-        {
-            Prof p(h, GPT2_K_GEMM_FWD, gemm_flops(BT, C, 4 * C), s);
-            HIPCHK(launch_gemm_nt(h->act<uint16_t>(la.gel), 4 * C, h->W(h->i_mat(l, 3)), 4 * C, BT, C, 4 * C,
-                                  h->P(h->i_vec(l, 7)), h->act<uint16_t>(la.xmid), C, h->act<uint16_t>(xnext), C, s));
-        }
+        HIPCHK(launch_layernorm_fwd(h->act<uint16_t>(la.x), h->P(h->i_vec(l, 0)), h->P(h->i_vec(l, 1)),
+                                    h->act<uint16_t>(la.ln1), h->act<float>(la.mean1), h->act<float>(la.rstd1), BT,
+                                    C, s));
+        HIPCHK(launch_gemm_nt(h->act<uint16_t>(la.ln1), C, h->W(h->i_mat(l, 0)), C, BT, 3 * C, C,
+                              h->P(h->i_vec(l, 2)), nullptr, 0, h->act<uint16_t>(la.qkv), 3 * C, s));
+        HIPCHK(launch_attention_fwd(h->act<uint16_t>(la.qkv), h->act<uint16_t>(la.att), h->act<float>(la.lse), c.B,
+                                    c.T, c.H, C, s));
+        HIPCHK(launch_gemm_nt(h->act<uint16_t>(la.att), C, h->W(h->i_mat(l, 1)), C, BT, C, C, h->P(h->i_vec(l, 3)),
+                              h->act<uint16_t>(la.x), C, h->act<uint16_t>(la.xmid), C, s));
+        HIPCHK(launch_layernorm_fwd(h->act<uint16_t>(la.xmid), h->P(h->i_vec(l, 4)), h->P(h->i_vec(l, 5)),
+                                    h->act<uint16_t>(la.ln2), h->act<float>(la.mean2), h->act<float>(la.rstd2), BT,
+                                    C, s));
+        HIPCHK(launch_gemm_nt_gelu(h->act<uint16_t>(la.ln2), C, h->W(h->i_mat(l, 2)), C, BT, 4 * C, C,
+                                   h->P(h->i_vec(l, 6)), h->act<uint16_t>(la.pre), h->act<uint16_t>(la.gel), 4 * C,
+                                   s));
+        HIPCHK(launch_gemm_nt(h->act<uint16_t>(la.gel), 4 * C, h->W(h->i_mat(l, 3)), 4 * C, BT, C, 4 * C,
+                              h->P(h->i_vec(l, 7)), h->act<uint16_t>(la.xmid), C, h->act<uint16_t>(xnext), C, s));
     }
-    {
-        Prof p(h, GPT2_K_LAYERNORM, 2.0 * BT * C * 2, s);
-        HIPCHK(launch_layernorm_fwd(h->act<uint16_t>(h->acts.xfinal), h->P(h->i_lnf(0)), h->P(h->i_lnf(1)),
-                                    h->act<uint16_t>(h->acts.lnf), h->act<float>(h->acts.meanf),
-                                    h->act<float>(h->acts.rstdf), BT, C, s));
-    }
-    {
-        Prof p(h, GPT2_K_GEMM_FWD, gemm_flops(BT, c.V, C), s, GPT2_K_LMHEAD_FWD);
-        HIPCHK(launch_gemm_nt(h->act<uint16_t>(h->acts.lnf), C, h->W(h->i_wte()), C, BT, c.Vp, C, nullptr, nullptr, 0,
-                              h->act<uint16_t>(h->acts.logits), c.Vp, s));
-    }
+    HIPCHK(launch_layernorm_fwd(h->act<uint16_t>(h->acts.xfinal), h->P(h->i_lnf(0)), h->P(h->i_lnf(1)),
+                                h->act<uint16_t>(h->acts.lnf), h->act<float>(h->acts.meanf),
+                                h->act<float>(h->acts.rstdf), BT, C, s));
+    HIPCHK(launch_gemm_nt(h->act<uint16_t>(h->acts.lnf), C, h->W(h->i_wte()), C, BT, c.Vp, C, nullptr, nullptr, 0,
+                          h->act<uint16_t>(h->acts.logits), c.Vp, s));
     if (tgt) {
-        {
-            Prof p(h, GPT2_K_XENT, (train ? 2.0 : 1.0) * BT * (double)c.Vp * 2, s);
-            HIPCHK(launch_xent(h->act<uint16_t>(h->acts.logits), tgt, h->act<float>(h->acts.loss_rows), BT, c.V, c.Vp,
-                               dloss, train ? 1 : 0, flag, s));
-        }
+        HIPCHK(launch_xent(h->act<uint16_t>(h->acts.logits), tgt, h->act<float>(h->acts.loss_rows), BT, c.V, c.Vp,
+                           dloss, train ? 1 : 0, flag, s));
         float* ldst = loss_dev ? loss_dev : (float*)(h->S() + h->scr.loss);
         HIPCHK(launch_mean(h->act<float>(h->acts.loss_rows), BT, ldst, s));
     }
@@ -338,89 +319,47 @@ int run_backward(gpt2_handle* h, hipStream_t s) {
     uint16_t* dlogits = h->act<uint16_t>(A.logits);
 
     // lm_head (tied): d_lnf = dlogits . wte ; dwte += dlogits^T . lnf
-    {
-        Prof p(h, GPT2_K_GEMM_DX, gemm_flops(BT, C, c.V), s);
-        HIPCHK(launch_gemm_nt(dlogits, c.Vp, h->WT(h->i_wte()), c.Vp, BT, C, c.Vp, nullptr, nullptr, 0, d_ln, C, s));
-    }
-    {
-        Prof p(h, GPT2_K_GEMM_DW, gemm_flops(BT, c.V, C), s);
-        HIPCHK(launch_gemm_tn_acc(dlogits, c.Vp, h->act<uint16_t>(A.lnf), C, BT, c.Vp, C, h->G(h->i_wte()), splitk,
-                                  splitk_n, s));
-    }
-    {
-        Prof p(h, GPT2_K_LAYERNORM, 3.0 * BT * C * 2, s);
-        HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(A.xfinal), d_ln, h->P(h->i_lnf(0)), h->act<float>(A.meanf),
-                                    h->act<float>(A.rstdf), d_res, 0, h->G(h->i_lnf(0)), h->G(h->i_lnf(1)), colp, BT, C,
-                                    s));
-    }
+    HIPCHK(launch_gemm_nt(dlogits, c.Vp, h->WT(h->i_wte()), c.Vp, BT, C, c.Vp, nullptr, nullptr, 0, d_ln, C, s));
+    HIPCHK(launch_gemm_tn_acc(dlogits, c.Vp, h->act<uint16_t>(A.lnf), C, BT, c.Vp, C, h->G(h->i_wte()), splitk,
+                              splitk_n, s));
+    HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(A.xfinal), d_ln, h->P(h->i_lnf(0)), h->act<float>(A.meanf),
+                                h->act<float>(A.rstdf), d_res, 0, h->G(h->i_lnf(0)), h->G(h->i_lnf(1)), colp, BT, C,
+                                s));
     for (int l = c.L - 1; l >= 0; --l) {
         const LayerActs& la = A.layer[l];
         // FC-proj: x_next = x_mid + gel . W_fp^T + b_fp
-        {
-            Prof p(h, GPT2_K_GEMM_DX, gemm_flops(BT, 4 * C, C), s);
-            HIPCHK(launch_gemm_nt(d_res, C, h->WT(h->i_mat(l, 3)), C, BT, 4 * C, C, nullptr, nullptr, 0, d_big, 4 * C,
-                                  s));
-        }
-        {
-            Prof p(h, GPT2_K_GEMM_DW, gemm_flops(BT, C, 4 * C), s);
-            HIPCHK(launch_gemm_tn_acc(d_res, C, h->act<uint16_t>(la.gel), 4 * C, BT, C, 4 * C, h->G(h->i_mat(l, 3)),
-                                      splitk, splitk_n, s));
-        }
+        HIPCHK(launch_gemm_nt(d_res, C, h->WT(h->i_mat(l, 3)), C, BT, 4 * C, C, nullptr, nullptr, 0, d_big, 4 * C,
+                              s));
+        HIPCHK(launch_gemm_tn_acc(d_res, C, h->act<uint16_t>(la.gel), 4 * C, BT, C, 4 * C, h->G(h->i_mat(l, 3)),
+                                  splitk, splitk_n, s));
         HIPCHK(launch_bias_grad(d_res, C, h->G(h->i_vec(l, 7)), colp, BT, C, s));
         // GELU backward + b_fc gradient
         HIPCHK(launch_bias_gelu_bwd(h->act<uint16_t>(la.pre), d_big, d_big, h->G(h->i_vec(l, 6)), colp, BT, 4 * C, s));
         // FC: pre = ln2 . W_fc^T + b_fc
-        {
-            Prof p(h, GPT2_K_GEMM_DX, gemm_flops(BT, C, 4 * C), s);
-            HIPCHK(launch_gemm_nt(d_big, 4 * C, h->WT(h->i_mat(l, 2)), 4 * C, BT, C, 4 * C, nullptr, nullptr, 0, d_ln, C,
-                                  s));
-        }
-        {
-            Prof p(h, GPT2_K_GEMM_DW, gemm_flops(BT, 4 * C, C), s);
-            HIPCHK(launch_gemm_tn_acc(d_big, 4 * C, h->act<uint16_t>(la.ln2), C, BT, 4 * C, C, h->G(h->i_mat(l, 2)),
-                                      splitk, splitk_n, s));
-        }
-        {
-            Prof p(h, GPT2_K_LAYERNORM, 3.0 * BT * C * 2, s);
-            HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(la.xmid), d_ln, h->P(h->i_vec(l, 4)), h->act<float>(la.mean2),
-                                        h->act<float>(la.rstd2), d_res, 1, h->G(h->i_vec(l, 4)), h->G(h->i_vec(l, 5)),
-                                        colp, BT, C, s));
-        }
+        HIPCHK(launch_gemm_nt(d_big, 4 * C, h->WT(h->i_mat(l, 2)), 4 * C, BT, C, 4 * C, nullptr, nullptr, 0, d_ln, C,
+                              s));
+        HIPCHK(launch_gemm_tn_acc(d_big, 4 * C, h->act<uint16_t>(la.ln2), C, BT, 4 * C, C, h->G(h->i_mat(l, 2)),
+                                  splitk, splitk_n, s));
+        HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(la.xmid), d_ln, h->P(h->i_vec(l, 4)), h->act<float>(la.mean2),
+                                    h->act<float>(la.rstd2), d_res, 1, h->G(h->i_vec(l, 4)), h->G(h->i_vec(l, 5)),
+                                    colp, BT, C, s));
         // attention projection: x_mid = x + att . W_p^T + b_p
-        {
-            Prof p(h, GPT2_K_GEMM_DX, gemm_flops(BT, C, C), s);
-            HIPCHK(launch_gemm_nt(d_res, C, h->WT(h->i_mat(l, 1)), C, BT, C, C, nullptr, nullptr, 0, d_att, C, s));
-        }
-        {
-            Prof p(h, GPT2_K_GEMM_DW, gemm_flops(BT, C, C), s);
-            HIPCHK(launch_gemm_tn_acc(d_res, C, h->act<uint16_t>(la.att), C, BT, C, C, h->G(h->i_mat(l, 1)), splitk,
-                                      splitk_n, s));
-        }
+        HIPCHK(launch_gemm_nt(d_res, C, h->WT(h->i_mat(l, 1)), C, BT, C, C, nullptr, nullptr, 0, d_att, C, s));
+        HIPCHK(launch_gemm_tn_acc(d_res, C, h->act<uint16_t>(la.att), C, BT, C, C, h->G(h->i_mat(l, 1)), splitk,
+                                  splitk_n, s));
         HIPCHK(launch_bias_grad(d_res, C, h->G(h->i_vec(l, 3)), colp, BT, C, s));
-        {
-            Prof p(h, GPT2_K_ATTN_BWD, attn_flops(c, 4), s);
-            HIPCHK(launch_attention_bwd(h->act<uint16_t>(la.qkv), h->act<uint16_t>(la.att), d_att,
-                                        h->act<float>(la.lse), d_qkv, (float*)(h->S() + h->scr.dvec), c.B, c.T, c.H, C,
-                                        s));
-        }
+        HIPCHK(launch_attention_bwd(h->act<uint16_t>(la.qkv), h->act<uint16_t>(la.att), d_att,
+                                    h->act<float>(la.lse), d_qkv, (float*)(h->S() + h->scr.dvec), c.B, c.T, c.H, C,
+                                    s));
         // QKV: qkv = ln1 . W_qkv^T + b_qkv
-        {
-            Prof p(h, GPT2_K_GEMM_DX, gemm_flops(BT, C, 3 * C), s);
-            HIPCHK(launch_gemm_nt(d_qkv, 3 * C, h->WT(h->i_mat(l, 0)), 3 * C, BT, C, 3 * C, nullptr, nullptr, 0, d_ln, C,
-                                  s));
-        }
-        {
-            Prof p(h, GPT2_K_GEMM_DW, gemm_flops(BT, 3 * C, C), s);
-            HIPCHK(launch_gemm_tn_acc(d_qkv, 3 * C, h->act<uint16_t>(la.ln1), C, BT, 3 * C, C, h->G(h->i_mat(l, 0)),
-                                      splitk, splitk_n, s));
-        }
+        HIPCHK(launch_gemm_nt(d_qkv, 3 * C, h->WT(h->i_mat(l, 0)), 3 * C, BT, C, 3 * C, nullptr, nullptr, 0, d_ln, C,
+                              s));
+        HIPCHK(launch_gemm_tn_acc(d_qkv, 3 * C, h->act<uint16_t>(la.ln1), C, BT, 3 * C, C, h->G(h->i_mat(l, 0)),
+                                  splitk, splitk_n, s));
         HIPCHK(launch_bias_grad(d_qkv, 3 * C, h->G(h->i_vec(l, 2)), colp, BT, 3 * C, s));
-        {
-            Prof p(h, GPT2_K_LAYERNORM, 3.0 * BT * C * 2, s);
-            HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(la.x), d_ln, h->P(h->i_vec(l, 0)), h->act<float>(la.mean1),
-                                        h->act<float>(la.rstd1), d_res, 1, h->G(h->i_vec(l, 0)), h->G(h->i_vec(l, 1)),
-                                        colp, BT, C, s));
-        }
+        HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(la.x), d_ln, h->P(h->i_vec(l, 0)), h->act<float>(la.mean1),
+                                    h->act<float>(la.rstd1), d_res, 1, h->G(h->i_vec(l, 0)), h->G(h->i_vec(l, 1)),
+                                    colp, BT, C, s));
     }
     HIPCHK(launch_embedding_bwd(h->last_tok, d_res, h->G(h->i_wte()), h->G(h->i_wpe()), c.B, c.T, C, c.V, s));
     return GPT2_OK;
@@ -529,11 +468,7 @@ int gpt2_init(const gpt2_config* cfg, uint64_t seed, const float* host_init, con
     }
     e = hipMemsetAsync(bufs->scratch, 0, 256, s);
     if (e != hipSuccess) return fail(e);
-    h->ev0.resize(PROF_MAX);
-    h->ev1.resize(PROF_MAX);
-    for (int i = 0; i < PROF_MAX; ++i) {
-        if (hipEventCreate(&h->ev0[i]) != hipSuccess || hipEventCreate(&h->ev1[i]) != hipSuccess) return fail(e);
-    }
+    h->sink.h = h;
     *out = h;
     return GPT2_OK;
 }
@@ -541,6 +476,7 @@ int gpt2_init(const gpt2_config* cfg, uint64_t seed, const float* host_init, con
 int gpt2_forward(gpt2_handle* h, const int32_t* tok, const int32_t* tgt, float dloss_scale, float* loss_dev,
                  hipStream_t s) {
     if (!h || !tok) return GPT2_E_INVALID;
+    SinkGuard guard(h);
     h->grad_ready = false;
     int r = run_forward(h, tok, tgt, dloss_scale, loss_dev, true, s);
     if (r == GPT2_OK && tgt) {
@@ -553,12 +489,14 @@ int gpt2_forward(gpt2_handle* h, const int32_t* tok, const int32_t* tgt, float d
 int gpt2_backward(gpt2_handle* h, hipStream_t s) {
     if (!h) return GPT2_E_INVALID;
     if (!h->grad_ready) return GPT2_E_STATE;
+    SinkGuard guard(h);
     h->grad_ready = false;
     return run_backward(h, s);
 }
 
 int gpt2_clip_adamw(gpt2_handle* h, const gpt2_adamw_args* a, float* grad_norm_dev, hipStream_t s) {
     if (!h || !a || a->t < 1 || !(a->max_norm > 0.0f)) return GPT2_E_INVALID;
+    SinkGuard guard(h);
     AdamwHostArgs ha;
     ha.lr = a->lr;
     ha.beta1 = a->beta1;
@@ -568,12 +506,9 @@ int gpt2_clip_adamw(gpt2_handle* h, const gpt2_adamw_args* a, float* grad_norm_d
     ha.max_norm = a->max_norm;
     ha.inv_bc1 = (float)(1.0 / (1.0 - std::pow((double)a->beta1, (double)a->t)));
     ha.inv_bc2 = (float)(1.0 / (1.0 - std::pow((double)a->beta2, (double)a->t)));
-    {
-        Prof p(h, GPT2_K_ADAMW, (double)h->n_params * 4 * 8 + (double)h->n_decay * 2, s);
-        HIPCHK(launch_clip_adamw(h->bufs.params, h->bufs.grads, h->bufs.m, h->bufs.v, h->bufs.shadow, h->n_params,
-                                 h->n_decay, ha, grad_norm_dev, (double*)(h->S() + h->scr.norm_partial),
-                                 (float*)(h->S() + h->scr.scale), s));
-    }
+    HIPCHK(launch_clip_adamw(h->bufs.params, h->bufs.grads, h->bufs.m, h->bufs.v, h->bufs.shadow, h->n_params,
+                             h->n_decay, ha, grad_norm_dev, (double*)(h->S() + h->scr.norm_partial),
+                             (float*)(h->S() + h->scr.scale), s));
     return refresh_shadow(h, s);
 }
 
@@ -581,7 +516,11 @@ int gpt2_eval_loss(gpt2_handle* h, const int32_t* tok, const int32_t* tgt, float
     if (!h || !tok || !tgt || !loss_host) return GPT2_E_INVALID;
     h->grad_ready = false;
     float* dev_loss = (float*)(h->S() + h->scr.loss);
-    int r = run_forward(h, tok, tgt, 0.0f, dev_loss, false, s);
+    int r;
+    {
+        SinkGuard guard(h);
+        r = run_forward(h, tok, tgt, 0.0f, dev_loss, false, s);
+    }
     if (r != GPT2_OK) return r;
     HIPCHK(hipMemcpyAsync(loss_host, dev_loss, sizeof(float), hipMemcpyDeviceToHost, s));
     return gpt2_sync_status(h, s);
@@ -629,28 +568,47 @@ const char* gpt2_strerror(int st) {
 }
 
 int gpt2_prof_enable(gpt2_handle* h, int32_t kclass) {
-    if (!h || kclass < 0 || kclass > GPT2_K_LMHEAD_FWD) return GPT2_E_INVALID;
+    if (!h || kclass < -1 || kclass >= KC_COUNT) return GPT2_E_INVALID;
+    if (kclass != 0 && h->ev0.empty()) {
+        h->ev0.resize(PROF_MAX);
+        h->ev1.resize(PROF_MAX);
+        for (int i = 0; i < PROF_MAX; ++i) {
+            HIPCHK(hipEventCreate(&h->ev0[i]));
+            HIPCHK(hipEventCreate(&h->ev1[i]));
+        }
+    }
     h->prof_class = kclass;
-    h->prof_n = 0;
-    h->prof_work = 0.0;
+    h->recs.clear();
     return GPT2_OK;
 }
 
-int gpt2_prof_read(gpt2_handle* h, hipStream_t s, double* total_ms, int64_t* launches, double* work) {
+int gpt2_prof_read(gpt2_handle* h, hipStream_t s, int32_t kclass, double* total_ms, int64_t* launches,
+                   double* work) {
     if (!h || !total_ms || !launches || !work) return GPT2_E_INVALID;
     HIPCHK(hipStreamSynchronize(s));
-    double tot = 0.0;
-    for (int i = 0; i < h->prof_n; ++i) {
+    double tot = 0.0, wk = 0.0;
+    int64_t n = 0;
+    for (size_t i = 0; i < h->recs.size(); ++i) {
+        if (kclass != -1 && h->recs[i].cls != kclass) continue;
         float ms = 0.f;
         HIPCHK(hipEventElapsedTime(&ms, h->ev0[i], h->ev1[i]));
         tot += ms;
+        wk += h->recs[i].work;
+        ++n;
     }
     *total_ms = tot;
-    *launches = h->prof_n;
-    *work = h->prof_work;
-    h->prof_n = 0;
-    h->prof_work = 0.0;
+    *launches = n;
+    *work = wk;
     return GPT2_OK;
+}
+
+const char* gpt2_prof_class_name(int32_t kclass) {
+    static const char* names[KC_COUNT] = {
+        "none", "gemm_nt", "gemm_nt_gelu", "gemm_tn_acc", "gemm_tn_splitk", "splitk_reduce", "attn_fwd",
+        "attn_dvec", "attn_dkdv", "attn_dq", "xent", "layernorm_fwd", "layernorm_bwd", "fold_partials",
+        "bias_gelu_bwd", "colsum", "embedding_fwd", "embedding_bwd_wte", "embedding_bwd_wpe", "sumsq",
+        "norm_finalize", "adamw", "transpose_bf16", "mean", "bias_gelu_fwd", "other"};
+    return (kclass >= 0 && kclass < KC_COUNT) ? names[kclass] : nullptr;
 }
 
 // ---------------------------------------------------------------- kernel-level entry points

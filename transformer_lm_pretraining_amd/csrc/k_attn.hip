@@ -17,6 +17,7 @@
 // reason, with Q^T and dO^T tiles in LDS.
 #include "common.h"
 #include "kernels.h"
+#include "prof.h"
 
 namespace {
 
@@ -402,11 +403,16 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(const uint16_t* __restrict
         }
 }
 
+// MFMA work executed over the causal pairs (t, s <= t): `matmuls` products of 2*D FLOP per pair.
+double attn_work(int B, int T, int H, int D, int matmuls) {
+    return (double)B * H * ((double)T * (T + 1) / 2.0) * 2.0 * D * matmuls;
+}
+
 template <int D>
 hipError_t fwd_t(const uint16_t* qkv, uint16_t* out, float* lse, int B, int T, int H, int C, hipStream_t s) {
     const float scale_log2 = LOG2E / sqrtf((float)D);
     dim3 grid((unsigned)cdiv(T, QB), (unsigned)(B * H));
-    hipLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(256), 0, s, qkv, out, lse, T, H, C, scale_log2);
+    PROF_LAUNCH(KC_ATTN_FWD, attn_work(B, T, H, D, 2), s, hipLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(256), 0, s, qkv, out, lse, T, H, C, scale_log2));
     return hipGetLastError();
 }
 
@@ -416,17 +422,17 @@ hipError_t bwd_t(const uint16_t* qkv, const uint16_t* out, const uint16_t* dout,
     const float scale = 1.0f / sqrtf((float)D);
     const float scale_log2 = LOG2E * scale;
     int64_t n = (int64_t)B * T * H;
-    hipLaunchKernelGGL(attn_dvec_kernel<D>, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 8192)), dim3(256), 0, s,
-                       out, dout, dvec, B, T, H, C);
+    PROF_LAUNCH(KC_ATTN_DVEC, 4.0 * (double)n * D, s, hipLaunchKernelGGL(attn_dvec_kernel<D>, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 8192)), dim3(256), 0, s,
+                       out, dout, dvec, B, T, H, C));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)cdiv(T, QB), (unsigned)(B * H));
-    hipLaunchKernelGGL(attn_dkdv_kernel<D>, grid, dim3(256), 0, s, qkv, dout, lse, dvec, dqkv, T, H, C, scale_log2,
-                       scale);
+    PROF_LAUNCH(KC_ATTN_DKDV, attn_work(B, T, H, D, 4), s, hipLaunchKernelGGL(attn_dkdv_kernel<D>, grid, dim3(256), 0, s, qkv, dout, lse, dvec, dqkv, T, H, C, scale_log2,
+                       scale));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_dq_kernel<D>, grid, dim3(256), 0, s, qkv, dout, lse, dvec, dqkv, T, H, C, scale_log2,
-                       scale);
+    PROF_LAUNCH(KC_ATTN_DQ, attn_work(B, T, H, D, 3), s, hipLaunchKernelGGL(attn_dq_kernel<D>, grid, dim3(256), 0, s, qkv, dout, lse, dvec, dqkv, T, H, C, scale_log2,
+                       scale));
     return hipGetLastError();
 }
 

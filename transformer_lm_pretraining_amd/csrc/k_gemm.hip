@@ -15,6 +15,7 @@
 // consecutive rows hit distinct banks.
 #include "common.h"
 #include "kernels.h"
+#include "prof.h"
 
 namespace {
 
@@ -215,12 +216,17 @@ __global__ void splitk_reduce_kernel(const float4* __restrict__ part, float4* __
     }
 }
 
+constexpr int gemm_class(bool a_t, int epi) {
+    return !a_t ? (epi == EPI_GELU ? KC_GEMM_NT_GELU : KC_GEMM_NT)
+                : (epi == EPI_F32_STORE ? KC_GEMM_TN_SPLIT : KC_GEMM_TN_ACC);
+}
+
 template <int BM, int BN, int WGM, int WGN, bool A_T, bool B_T, int EPI>
 hipError_t run(GemmParams p, int splits, hipStream_t s) {
     p.tiles_m = (int)cdiv(p.M, BM);
     p.tiles_n = (int)cdiv(p.N, BN);
     dim3 grid(p.tiles_m * p.tiles_n, splits);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WGM, WGN, A_T, B_T, EPI>), grid, dim3(NTHREADS), 0, s, p);
+    PROF_LAUNCH(gemm_class(A_T, EPI), 2.0 * p.M * p.N * (double)p.k_len * splits, s, hipLaunchKernelGGL((gemm_kernel<BM, BN, WGM, WGN, A_T, B_T, EPI>), grid, dim3(NTHREADS), 0, s, p));
     return hipGetLastError();
 }
 
@@ -273,7 +279,7 @@ hipError_t launch_gemm_tn_acc(const uint16_t* dY, int64_t ldy, const uint16_t* X
     if (e != hipSuccess) return e;
     int64_t n4 = (int64_t)N * K / 4;
     int blocks = (int)std::min<int64_t>(cdiv(n4, 256), 4096);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, (const float4*)partial, (float4*)dW, n4,
-                       splits, n4);
+    PROF_LAUNCH(KC_SPLITK_REDUCE, 4.0 * n4 * 4 * (splits + 2), s, hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, (const float4*)partial, (float4*)dW, n4,
+                       splits, n4));
     return hipGetLastError();
 }

@@ -4,6 +4,7 @@
 // (8 bf16) per lane and keep fp32 arithmetic (PDS §4 precision paragraph).
 #include "common.h"
 #include "kernels.h"
+#include "prof.h"
 
 namespace {
 
@@ -274,8 +275,8 @@ hipError_t launch_bias_gelu_fwd(const uint16_t* u, const float* b, uint16_t* pre
                                 hipStream_t s) {
     int64_t nvec = rows * (N / 8);
     if (nvec <= 0) return hipSuccess;
-    hipLaunchKernelGGL(bias_gelu_fwd_kernel, dim3(grid_for(nvec)), dim3(256), 0, s, (const u32x4*)u, b, (u32x4*)pre,
-                       (u32x4*)g, nvec, N / 8);
+    PROF_LAUNCH(KC_BIAS_GELU_FWD, 48.0 * nvec, s, hipLaunchKernelGGL(bias_gelu_fwd_kernel, dim3(grid_for(nvec)), dim3(256), 0, s, (const u32x4*)u, b, (u32x4*)pre,
+                       (u32x4*)g, nvec, N / 8));
     return hipGetLastError();
 }
 
@@ -286,11 +287,11 @@ hipError_t launch_bias_gelu_bwd(const uint16_t* pre, const uint16_t* dg, uint16_
     if (rows <= 0) return hipSuccess;
     if (N % 8 || N > 8 * CS_THREADS * CS_MAXV) return hipErrorInvalidValue;
     int blocks = colsum_blocks(rows);
-    hipLaunchKernelGGL(colsum_kernel<true>, dim3(blocks), dim3(CS_THREADS), 0, s, dg, (int64_t)N, pre, dpre, partial,
-                       rows, N);
+    PROF_LAUNCH(KC_GELU_BWD, 6.0 * rows * N, s, hipLaunchKernelGGL(colsum_kernel<true>, dim3(blocks), dim3(CS_THREADS), 0, s, dg, (int64_t)N, pre, dpre, partial,
+                       rows, N));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fold_colsum_kernel, dim3(cdiv(N, 256)), dim3(256), 0, s, partial, blocks, N, db);
+    PROF_LAUNCH(KC_FOLD, 4.0 * blocks * N, s, hipLaunchKernelGGL(fold_colsum_kernel, dim3(cdiv(N, 256)), dim3(256), 0, s, partial, blocks, N, db));
     return hipGetLastError();
 }
 
@@ -299,8 +300,8 @@ hipError_t launch_bias_grad(const uint16_t* dY, int64_t ldy, float* db, float* p
     if (rows <= 0) return hipSuccess;
     if (N % 8 || N > 8 * CS_THREADS * CS_MAXV) return hipErrorInvalidValue;
     int blocks = colsum_blocks(rows);
-    hipLaunchKernelGGL(colsum_kernel<false>, dim3(blocks), dim3(CS_THREADS), 0, s, dY, ldy, (const uint16_t*)nullptr,
-                       (uint16_t*)nullptr, partial, rows, N);
+    PROF_LAUNCH(KC_COLSUM, 2.0 * rows * N, s, hipLaunchKernelGGL(colsum_kernel<false>, dim3(blocks), dim3(CS_THREADS), 0, s, dY, ldy, (const uint16_t*)nullptr,
+                       (uint16_t*)nullptr, partial, rows, N));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fold_colsum_kernel, dim3(cdiv(N, 256)), dim3(256), 0, s, partial, blocks, N, db);
@@ -314,7 +315,7 @@ hipError_t launch_xent(uint16_t* logits, const int32_t* tgt, float* loss_rows, i
     dim3 grid((unsigned)rows), block(XE_THREADS);
     switch (nv) {
 #define XE(n) \
-    case n: hipLaunchKernelGGL(xent_kernel<n>, grid, block, 0, s, logits, tgt, loss_rows, V, Vp, dloss, write_grad, flag); break;
+    case n: PROF_LAUNCH(KC_XENT, 2.0 * rows * Vp * (write_grad ? 2 : 1), s, hipLaunchKernelGGL(xent_kernel<n>, grid, block, 0, s, logits, tgt, loss_rows, V, Vp, dloss, write_grad, flag)); break;
         XE(1) XE(2) XE(3) XE(4) XE(5) XE(6) XE(7) XE(8) XE(9) XE(10) XE(11) XE(12) XE(13) XE(14) XE(15) XE(16)
 #undef XE
         default: return hipErrorInvalidValue;
@@ -323,25 +324,25 @@ hipError_t launch_xent(uint16_t* logits, const int32_t* tgt, float* loss_rows, i
 }
 
 hipError_t launch_mean(const float* x, int64_t n, float* out, hipStream_t s) {
-    hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(1024), 0, s, x, n, out);
+    PROF_LAUNCH(KC_MEAN, 4.0 * n, s, hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(1024), 0, s, x, n, out));
     return hipGetLastError();
 }
 
 hipError_t launch_embedding_fwd(const int32_t* tok, const uint16_t* wte, const uint16_t* wpe, uint16_t* x, int B,
                                 int T, int C, int V, int32_t* flag, hipStream_t s) {
     int64_t rows = (int64_t)B * T;
-    hipLaunchKernelGGL(embedding_fwd_kernel, dim3(grid_for(rows * (C / 8))), dim3(256), 0, s, tok, wte, wpe, x, rows,
-                       T, C, V, flag);
+    PROF_LAUNCH(KC_EMB_FWD, 6.0 * rows * C, s, hipLaunchKernelGGL(embedding_fwd_kernel, dim3(grid_for(rows * (C / 8))), dim3(256), 0, s, tok, wte, wpe, x, rows,
+                       T, C, V, flag));
     return hipGetLastError();
 }
 
 hipError_t launch_embedding_bwd(const int32_t* tok, const uint16_t* dx, float* dwte, float* dwpe, int B, int T,
                                 int C, int V, hipStream_t s) {
     int64_t rows = (int64_t)B * T;
-    hipLaunchKernelGGL(embedding_bwd_wte_kernel, dim3(grid_for(rows * (C / 8))), dim3(256), 0, s, tok, dx, dwte, rows,
-                       C, V);
+    PROF_LAUNCH(KC_EMB_BWD_WTE, 10.0 * rows * C, s, hipLaunchKernelGGL(embedding_bwd_wte_kernel, dim3(grid_for(rows * (C / 8))), dim3(256), 0, s, tok, dx, dwte, rows,
+                       C, V));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(embedding_bwd_wpe_kernel, dim3(grid_for((int64_t)T * C)), dim3(256), 0, s, dx, dwpe, B, T, C);
+    PROF_LAUNCH(KC_EMB_BWD_WPE, 2.0 * rows * C + 8.0 * T * C, s, hipLaunchKernelGGL(embedding_bwd_wpe_kernel, dim3(grid_for((int64_t)T * C)), dim3(256), 0, s, dx, dwpe, B, T, C));
     return hipGetLastError();
 }

@@ -7,6 +7,7 @@
 // which a second small kernel folds into dw, db.
 #include "common.h"
 #include "kernels.h"
+#include "prof.h"
 
 namespace {
 
@@ -167,8 +168,9 @@ int ln_blocks(int64_t rows) { return (int)std::min<int64_t>(512, cdiv(rows, ROWS
 template <int VEC, int NV>
 hipError_t ln_fwd_t(const uint16_t* x, const float* w, const float* b, uint16_t* y, float* mean, float* rstd,
                     int64_t rows, hipStream_t s) {
-    hipLaunchKernelGGL((ln_fwd_kernel<VEC, NV>), dim3(cdiv(rows, ROWS_PER_BLOCK)), dim3(256), 0, s, x, w, b, y, mean,
-                       rstd, rows);
+    constexpr int C = NV * 64 * VEC;
+    PROF_LAUNCH(KC_LN_FWD, 4.0 * rows * C, s, hipLaunchKernelGGL((ln_fwd_kernel<VEC, NV>), dim3(cdiv(rows, ROWS_PER_BLOCK)), dim3(256), 0, s, x, w, b, y, mean,
+                       rstd, rows));
     return hipGetLastError();
 }
 
@@ -178,11 +180,11 @@ hipError_t ln_bwd_t(const uint16_t* x, const uint16_t* dy, const float* w, const
                     hipStream_t s) {
     constexpr int C = NV * 64 * VEC;
     int blocks = ln_blocks(rows);
-    hipLaunchKernelGGL((ln_bwd_kernel<VEC, NV>), dim3(blocks), dim3(256), 0, s, x, dy, w, mean, rstd, dres,
-                       accumulate, partial, rows);
+    PROF_LAUNCH(KC_LN_BWD, 2.0 * rows * C * (accumulate ? 4 : 3), s, hipLaunchKernelGGL((ln_bwd_kernel<VEC, NV>), dim3(blocks), dim3(256), 0, s, x, dy, w, mean, rstd, dres,
+                       accumulate, partial, rows));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fold_partials_kernel, dim3(cdiv(2 * C, 256)), dim3(256), 0, s, partial, blocks, C, 2, dw, db);
+    PROF_LAUNCH(KC_FOLD, 8.0 * blocks * C, s, hipLaunchKernelGGL(fold_partials_kernel, dim3(cdiv(2 * C, 256)), dim3(256), 0, s, partial, blocks, C, 2, dw, db));
     return hipGetLastError();
 }
 

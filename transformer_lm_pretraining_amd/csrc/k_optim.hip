@@ -5,6 +5,7 @@
 // maintenance.  All HBM-bound: float4 vectors, grid-stride loops.
 #include "common.h"
 #include "kernels.h"
+#include "prof.h"
 
 namespace {
 
@@ -151,41 +152,41 @@ hipError_t launch_clip_adamw(float* p, float* g, float* m, float* v, uint16_t* s
                              const AdamwHostArgs& a, float* norm_dev, double* partial, float* scale_dev,
                              hipStream_t s) {
     const int64_t n4 = n / 4;
-    hipLaunchKernelGGL(sumsq_kernel, dim3(NORM_BLOCKS), dim3(OPT_THREADS), 0, s, (const float4*)g, n4, partial);
+    PROF_LAUNCH(KC_SUMSQ, 4.0 * n, s, hipLaunchKernelGGL(sumsq_kernel, dim3(NORM_BLOCKS), dim3(OPT_THREADS), 0, s, (const float4*)g, n4, partial));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(norm_finalize_kernel, dim3(1), dim3(OPT_THREADS), 0, s, partial, NORM_BLOCKS, a.max_norm,
-                       scale_dev, norm_dev);
+    PROF_LAUNCH(KC_NORM_FINAL, 8.0 * NORM_BLOCKS, s, hipLaunchKernelGGL(norm_finalize_kernel, dim3(1), dim3(OPT_THREADS), 0, s, partial, NORM_BLOCKS, a.max_norm,
+                       scale_dev, norm_dev));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     AdamwDev d{a.lr, a.beta1, a.beta2, a.eps, a.wd, a.inv_bc1, a.inv_bc2};
-    hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(n4, 8192)), dim3(OPT_THREADS), 0, s, (float4*)p, (float4*)g,
-                       (float4*)m, (float4*)v, (uint2*)shadow, n4, n_decay / 4, d, (const float*)scale_dev);
+    PROF_LAUNCH(KC_ADAMW, 32.0 * n + 2.0 * n_decay, s, hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(n4, 8192)), dim3(OPT_THREADS), 0, s, (float4*)p, (float4*)g,
+                       (float4*)m, (float4*)v, (uint2*)shadow, n4, n_decay / 4, d, (const float*)scale_dev));
     return hipGetLastError();
 }
 
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {
-    hipLaunchKernelGGL(cast_bf16_kernel, dim3(grid_for(n / 4)), dim3(OPT_THREADS), 0, s, (const float4*)src,
-                       (uint2*)dst, n / 4);
+    PROF_LAUNCH(KC_OTHER, 6.0 * n, s, hipLaunchKernelGGL(cast_bf16_kernel, dim3(grid_for(n / 4)), dim3(OPT_THREADS), 0, s, (const float4*)src,
+                       (uint2*)dst, n / 4));
     return hipGetLastError();
 }
 
 hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int R, int Cc, hipStream_t s) {
     dim3 grid((unsigned)cdiv(Cc, 64), (unsigned)cdiv(R, 64));
-    hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, src, dst, R, Cc);
+    PROF_LAUNCH(KC_TRANSPOSE, 4.0 * R * Cc, s, hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, src, dst, R, Cc));
     return hipGetLastError();
 }
 
 hipError_t launch_fill_f32(float* dst, float val, int64_t n, hipStream_t s) {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_for(n)), dim3(256), 0, s, dst, val, n);
+    PROF_LAUNCH(KC_OTHER, 4.0 * n, s, hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_for(n)), dim3(256), 0, s, dst, val, n));
     return hipGetLastError();
 }
 
 hipError_t launch_init_normal(float* dst, int64_t n, uint64_t seed, int tensor, double stdv, int64_t zero_from,
                               hipStream_t s) {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(init_normal_kernel, dim3(grid_for(n)), dim3(256), 0, s, dst, n, seed,
-                       (uint64_t)tensor << 40, stdv, zero_from);
+    PROF_LAUNCH(KC_OTHER, 4.0 * n, s, hipLaunchKernelGGL(init_normal_kernel, dim3(grid_for(n)), dim3(256), 0, s, dst, n, seed,
+                       (uint64_t)tensor << 40, stdv, zero_from));
     return hipGetLastError();
 }

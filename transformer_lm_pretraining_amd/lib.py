@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgpt2mi.so")
 
 GPT2_OK, GPT2_E_INVALID, GPT2_E_SHAPE, GPT2_E_STATE, GPT2_E_HIP, GPT2_E_DATA, GPT2_E_UNSUPPORTED = range(7)
-K_GEMM_FWD, K_GEMM_DX, K_GEMM_DW, K_ATTN_FWD, K_ATTN_BWD, K_XENT, K_LAYERNORM, K_ADAMW, K_LMHEAD_FWD = range(1, 10)
+# kernel classes whose work is counted in FLOP (the others count bytes)
+MFMA_CLASSES = ("gemm_nt", "gemm_nt_gelu", "gemm_tn_acc", "gemm_tn_splitk", "attn_fwd", "attn_dkdv", "attn_dq")
 
 
 class Gpt2Error(RuntimeError):
@@ -68,7 +69,9 @@ _SIGS = {
     "gpt2_destroy": (None, [c_void_p]),
     "gpt2_strerror": (ctypes.c_char_p, [c_int32]),
     "gpt2_prof_enable": (c_int32, [c_void_p, c_int32]),
-    "gpt2_prof_read": (c_int32, [c_void_p, c_void_p, POINTER(c_double), POINTER(c_int64), POINTER(c_double)]),
+    "gpt2_prof_read": (c_int32, [c_void_p, c_void_p, c_int32, POINTER(c_double), POINTER(c_int64),
+                                 POINTER(c_double)]),
+    "gpt2_prof_class_name": (ctypes.c_char_p, [c_int32]),
     "gpt2k_xent": (c_int32, [c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_int32, c_float, c_int32, c_void_p,
                              c_void_p]),
     "gpt2k_layernorm_fwd": (c_int32, [c_void_p] * 6 + [c_int64, c_int32, c_void_p]),
@@ -245,11 +248,24 @@ class GPT2:
     def prof_enable(self, kclass):
         check(self.lib.gpt2_prof_enable(self.h, kclass), "gpt2_prof_enable")
 
-    def prof_read(self):
+    def prof_read(self, kclass=-1):
+        """(total ms, launches, algorithmic work) over the recorded launches of kclass (-1: all)."""
         ms, n, work = c_double(), c_int64(), c_double()
-        check(self.lib.gpt2_prof_read(self.h, _stream(), ctypes.byref(ms), ctypes.byref(n), ctypes.byref(work)),
-              "gpt2_prof_read")
+        check(self.lib.gpt2_prof_read(self.h, _stream(), kclass, ctypes.byref(ms), ctypes.byref(n),
+                                      ctypes.byref(work)), "gpt2_prof_read")
         return ms.value, n.value, work.value
+
+
+def kernel_class_names():
+    """{class id: kernel name} of the timing classes."""
+    lib = load()
+    out = {}
+    for k in range(1, 64):
+        n = lib.gpt2_prof_class_name(k)
+        if n is None:
+            break
+        out[k] = n.decode()
+    return out
 
 
 # ---------------------------------------------------------------- kernel-level calls
