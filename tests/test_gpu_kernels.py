@@ -186,12 +186,33 @@ def test_gemm_tn_acc_parity(gpu_lib, M, N, K):
     dY = bf16_round(synth.normal((M, N), std=0.1, seed=71))
     X = bf16_round(synth.normal((M, K), seed=72))
     dW0 = synth.normal((N, K), std=0.3, seed=73).astype(np.float64)
+    db0 = synth.normal((N,), std=0.3, seed=74).astype(np.float64)
     dW = to_dev_f32(dW0)
-    lib.gemm_tn_acc(to_dev_bf16(dY), to_dev_bf16(X), dW)
+    db = to_dev_f32(db0)
+    lib.gemm_tn_acc(to_dev_bf16(dY), to_dev_bf16(X), dW, db)
     torch.cuda.synchronize()
     ref = dY.T @ X
     got = host(dW) - dW0.astype(np.float32)
     assert rel_l2(got, ref) <= 1e-4
+    np.testing.assert_allclose(host(db) - db0.astype(np.float32), dY.sum(0), rtol=1e-4, atol=1e-3)
+    # without the bias pointer the weight gradient alone accumulates
+    dW2 = to_dev_f32(np.zeros((N, K)))
+    lib.gemm_tn_acc(to_dev_bf16(dY), to_dev_bf16(X), dW2)
+    torch.cuda.synchronize()
+    assert rel_l2(host(dW2), ref) <= 1e-4
+
+
+def test_gemm_nt_dgelu_parity(gpu_lib):
+    import torch
+    from transformer_lm_pretraining_amd import lib
+    M, N, K = 515, 3072, 768
+    say("gemm_nt_dgelu", M, N, K)
+    A = bf16_round(synth.normal((M, K), seed=65))
+    B = bf16_round(synth.normal((N, K), std=0.05, seed=66))
+    pre = bf16_round(synth.normal((M, N), seed=67))
+    out = lib.gemm_nt_dgelu(to_dev_bf16(A), to_dev_bf16(B), to_dev_bf16(pre))
+    torch.cuda.synchronize()
+    assert rel_l2(host(out), ops.gelu_bwd(pre, A @ B.T)) <= 5e-3
 
 
 # ---------------------------------------------------------------- attention

@@ -320,34 +320,31 @@ int run_backward(gpt2_handle* h, hipStream_t s) {
 
     // lm_head (tied): d_lnf = dlogits . wte ; dwte += dlogits^T . lnf
     HIPCHK(launch_gemm_nt(dlogits, c.Vp, h->WT(h->i_wte()), c.Vp, BT, C, c.Vp, nullptr, nullptr, 0, d_ln, C, s));
-    HIPCHK(launch_gemm_tn_acc(dlogits, c.Vp, h->act<uint16_t>(A.lnf), C, BT, c.Vp, C, h->G(h->i_wte()), splitk,
-                              splitk_n, s));
+    HIPCHK(launch_gemm_tn_acc(dlogits, c.Vp, h->act<uint16_t>(A.lnf), C, BT, c.Vp, C, h->G(h->i_wte()), nullptr,
+                              splitk, splitk_n, s));
     HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(A.xfinal), d_ln, h->P(h->i_lnf(0)), h->act<float>(A.meanf),
                                 h->act<float>(A.rstdf), d_res, 0, h->G(h->i_lnf(0)), h->G(h->i_lnf(1)), colp, BT, C,
                                 s));
     for (int l = c.L - 1; l >= 0; --l) {
         const LayerActs& la = A.layer[l];
-        // FC-proj: x_next = x_mid + gel . W_fp^T + b_fp
-        HIPCHK(launch_gemm_nt(d_res, C, h->WT(h->i_mat(l, 3)), C, BT, 4 * C, C, nullptr, nullptr, 0, d_big, 4 * C,
-                              s));
+        // FC-proj: x_next = x_mid + gel . W_fp^T + b_fp.  The input gradient is taken
+        // through GELU in the GEMM epilogue (d_big = dpre); b_fp's gradient rides on the dW pass.
+        HIPCHK(launch_gemm_nt_dgelu(d_res, C, h->WT(h->i_mat(l, 3)), C, BT, 4 * C, C, h->act<uint16_t>(la.pre), d_big,
+                                    4 * C, s));
         HIPCHK(launch_gemm_tn_acc(d_res, C, h->act<uint16_t>(la.gel), 4 * C, BT, C, 4 * C, h->G(h->i_mat(l, 3)),
-                                  splitk, splitk_n, s));
-        HIPCHK(launch_bias_grad(d_res, C, h->G(h->i_vec(l, 7)), colp, BT, C, s));
-        // GELU backward + b_fc gradient
-        HIPCHK(launch_bias_gelu_bwd(h->act<uint16_t>(la.pre), d_big, d_big, h->G(h->i_vec(l, 6)), colp, BT, 4 * C, s));
+                                  h->G(h->i_vec(l, 7)), splitk, splitk_n, s));
         // FC: pre = ln2 . W_fc^T + b_fc
         HIPCHK(launch_gemm_nt(d_big, 4 * C, h->WT(h->i_mat(l, 2)), 4 * C, BT, C, 4 * C, nullptr, nullptr, 0, d_ln, C,
                               s));
         HIPCHK(launch_gemm_tn_acc(d_big, 4 * C, h->act<uint16_t>(la.ln2), C, BT, 4 * C, C, h->G(h->i_mat(l, 2)),
-                                  splitk, splitk_n, s));
+                                  h->G(h->i_vec(l, 6)), splitk, splitk_n, s));
         HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(la.xmid), d_ln, h->P(h->i_vec(l, 4)), h->act<float>(la.mean2),
                                     h->act<float>(la.rstd2), d_res, 1, h->G(h->i_vec(l, 4)), h->G(h->i_vec(l, 5)),
                                     colp, BT, C, s));
         // attention projection: x_mid = x + att . W_p^T + b_p
         HIPCHK(launch_gemm_nt(d_res, C, h->WT(h->i_mat(l, 1)), C, BT, C, C, nullptr, nullptr, 0, d_att, C, s));
-        HIPCHK(launch_gemm_tn_acc(d_res, C, h->act<uint16_t>(la.att), C, BT, C, C, h->G(h->i_mat(l, 1)), splitk,
-                                  splitk_n, s));
-        HIPCHK(launch_bias_grad(d_res, C, h->G(h->i_vec(l, 3)), colp, BT, C, s));
+        HIPCHK(launch_gemm_tn_acc(d_res, C, h->act<uint16_t>(la.att), C, BT, C, C, h->G(h->i_mat(l, 1)),
+                                  h->G(h->i_vec(l, 3)), splitk, splitk_n, s));
         HIPCHK(launch_attention_bwd(h->act<uint16_t>(la.qkv), h->act<uint16_t>(la.att), d_att,
                                     h->act<float>(la.lse), d_qkv, (float*)(h->S() + h->scr.dvec), c.B, c.T, c.H, C,
                                     s));
@@ -355,8 +352,7 @@ int run_backward(gpt2_handle* h, hipStream_t s) {
         HIPCHK(launch_gemm_nt(d_qkv, 3 * C, h->WT(h->i_mat(l, 0)), 3 * C, BT, C, 3 * C, nullptr, nullptr, 0, d_ln, C,
                               s));
         HIPCHK(launch_gemm_tn_acc(d_qkv, 3 * C, h->act<uint16_t>(la.ln1), C, BT, 3 * C, C, h->G(h->i_mat(l, 0)),
-                                  splitk, splitk_n, s));
-        HIPCHK(launch_bias_grad(d_qkv, 3 * C, h->G(h->i_vec(l, 2)), colp, BT, 3 * C, s));
+                                  h->G(h->i_vec(l, 2)), splitk, splitk_n, s));
         HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(la.x), d_ln, h->P(h->i_vec(l, 0)), h->act<float>(la.mean1),
                                     h->act<float>(la.rstd1), d_res, 1, h->G(h->i_vec(l, 0)), h->G(h->i_vec(l, 1)),
                                     colp, BT, C, s));
@@ -607,7 +603,7 @@ const char* gpt2_prof_class_name(int32_t kclass) {
         "none", "gemm_nt", "gemm_nt_gelu", "gemm_tn_acc", "gemm_tn_splitk", "splitk_reduce", "attn_fwd",
         "attn_dvec", "attn_dkdv", "attn_dq", "xent", "layernorm_fwd", "layernorm_bwd", "fold_partials",
         "bias_gelu_bwd", "colsum", "embedding_fwd", "embedding_bwd_wte", "embedding_bwd_wpe", "sumsq",
-        "norm_finalize", "adamw", "transpose_bf16", "mean", "bias_gelu_fwd", "other"};
+        "norm_finalize", "adamw", "transpose_bf16", "mean", "bias_gelu_fwd", "gemm_nt_dgelu", "other"};
     return (kclass >= 0 && kclass < KC_COUNT) ? names[kclass] : nullptr;
 }
 
@@ -696,11 +692,20 @@ int gpt2k_gemm_nt_gelu(const uint16_t* A, const uint16_t* B, const float* bias, 
     return GPT2_OK;
 }
 
-int gpt2k_gemm_tn_acc(const uint16_t* dY, const uint16_t* X, float* dW, void* scratch, int64_t scratch_bytes,
-                      int64_t M, int64_t N, int64_t K, hipStream_t s) {
+int gpt2k_gemm_nt_dgelu(const uint16_t* A, const uint16_t* B, const uint16_t* pre, uint16_t* out, int64_t M,
+                        int64_t N, int64_t K, hipStream_t s) {
+    if (!A || !B || !pre || !out || M < 1 || N < 1 || K < 64 || K % 64 || N % 8 || M > INT32_MAX)
+        return GPT2_E_INVALID;
+    KCHK(launch_gemm_nt_dgelu(A, K, B, K, (int)M, (int)N, (int)K, pre, out, N, s));
+    return GPT2_OK;
+}
+
+int gpt2k_gemm_tn_acc(const uint16_t* dY, const uint16_t* X, float* dW, float* db, void* scratch,
+                      int64_t scratch_bytes, int64_t M, int64_t N, int64_t K, hipStream_t s) {
     if (!dY || !X || !dW || M < 64 || M % 64 || N < 8 || N % 8 || K < 8 || K % 8 || M > INT32_MAX)
         return GPT2_E_INVALID;
-    KCHK(launch_gemm_tn_acc(dY, N, X, K, (int)M, (int)N, (int)K, dW, (float*)scratch, scratch ? scratch_bytes / 4 : 0,
+    KCHK(launch_gemm_tn_acc(dY, N, X, K, (int)M, (int)N, (int)K, dW, db, (float*)scratch,
+                            scratch ? scratch_bytes / 4 : 0,
                             s));
     return GPT2_OK;
 }

@@ -88,17 +88,25 @@ __device__ __forceinline__ void transpose8x8(const u32x4* in, u32x4* out) {
     }
 }
 
+// tanh(a) = 1 - 2 / (exp(2a) + 1), with the hardware base-2 exponential; |a| is
+// clamped at 15 where tanh is 1 to fp32 precision (keeps exp finite).
+__device__ __forceinline__ float fast_tanh(float a) {
+    a = fminf(fmaxf(a, -15.0f), 15.0f);
+    const float e = __builtin_amdgcn_exp2f(a * 2.8853900817779268f);  // exp(2a) = 2^(2a log2 e)
+    return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+}
+
 // GPT-2's tanh-form GELU and its derivative, evaluated in fp32.
 __device__ __forceinline__ float gelu_f(float x) {
     const float k = 0.7978845608028654f;  // sqrt(2/pi)
     float a = k * (x + 0.044715f * x * x * x);
-    return 0.5f * x * (1.0f + tanhf(a));
+    return 0.5f * x * (1.0f + fast_tanh(a));
 }
 __device__ __forceinline__ float gelu_grad_f(float x) {
     const float k = 0.7978845608028654f;
     float x2 = x * x;
     float a = k * (x + 0.044715f * x2 * x);
-    float t = tanhf(a);
+    float t = fast_tanh(a);
     return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * k * (1.0f + 3.0f * 0.044715f * x2);
 }
 

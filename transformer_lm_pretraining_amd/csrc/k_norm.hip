@@ -149,18 +149,27 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const uint16_t* __restrict_
     }
 }
 
-// out0[c] += sum_b partial[b][0][c], out1[c] += sum_b partial[b][1][c] (out1 may be null
-// when the partial rows hold a single array: then nparts arrays of width C).
-__global__ void fold_partials_kernel(const float* __restrict__ partial, int nblocks, int C, int arrays,
-                                     float* __restrict__ out0, float* __restrict__ out1) {
-    int c = blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= arrays * C) return;
-    double s = 0.0;
-    for (int b = 0; b < nblocks; ++b) s += partial[(int64_t)b * arrays * C + c];
+// out0[c] += sum_b partial[b][0][c], out1[c] += sum_b partial[b][1][c].  Block
+// (x, y) sums partial rows y, y + FOLD_SEGS, ... for 256 columns (coalesced
+// loads, 8 independent accumulators) and adds its segment sum atomically, so
+// the fold runs FOLD_SEGS-way parallel over the rows.
+constexpr int FOLD_SEGS = 16;
+__global__ __launch_bounds__(256) void fold_partials_kernel(const float* __restrict__ partial, int nblocks, int C,
+                                                            float* __restrict__ out0, float* __restrict__ out1) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= 2 * C) return;
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int b = blockIdx.y;
+    for (; b + 7 * FOLD_SEGS < nblocks; b += 8 * FOLD_SEGS) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s[u] += partial[(int64_t)(b + u * FOLD_SEGS) * 2 * C + c];
+    }
+    for (; b < nblocks; b += FOLD_SEGS) s[0] += partial[(int64_t)b * 2 * C + c];
+    const float t = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
     if (c < C)
-        out0[c] += (float)s;
+        unsafeAtomicAdd(out0 + c, t);
     else
-        out1[c - C] += (float)s;
+        unsafeAtomicAdd(out1 + c - C, t);
 }
 
 int ln_blocks(int64_t rows) { return (int)std::min<int64_t>(512, cdiv(rows, ROWS_PER_BLOCK)); }
@@ -184,7 +193,9 @@ hipError_t ln_bwd_t(const uint16_t* x, const uint16_t* dy, const float* w, const
                        accumulate, partial, rows));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    PROF_LAUNCH(KC_FOLD, 8.0 * blocks * C, s, hipLaunchKernelGGL(fold_partials_kernel, dim3(cdiv(2 * C, 256)), dim3(256), 0, s, partial, blocks, C, 2, dw, db));
+    PROF_LAUNCH(KC_FOLD, 8.0 * blocks * C, s,
+                hipLaunchKernelGGL(fold_partials_kernel, dim3(cdiv(2 * C, 256), FOLD_SEGS), dim3(256), 0, s, partial,
+                                   blocks, C, dw, db));
     return hipGetLastError();
 }
 

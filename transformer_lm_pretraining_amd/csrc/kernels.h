@@ -14,9 +14,13 @@ hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int
 // pre = A . B^T + bias; g = GELU(pre).
 hipError_t launch_gemm_nt_gelu(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M, int N, int K,
                                const float* bias, uint16_t* pre, uint16_t* g, int64_t ldo, hipStream_t s);
-// dW[N,K] += sum_m dY[m,n] X[m,k]; M % 64 == 0, N % 8 == 0, K % 8 == 0.
+// out = (A . B^T) * GELU'(pre), all bf16 [M, N] with leading dim ldo.
+hipError_t launch_gemm_nt_dgelu(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M, int N, int K,
+                                const uint16_t* pre, uint16_t* out, int64_t ldo, hipStream_t s);
+// dW[N,K] += sum_m dY[m,n] X[m,k]; dbias[n] += sum_m dY[m,n] if dbias != null.
+// M % 64 == 0, N % 8 == 0, K % 8 == 0.
 hipError_t launch_gemm_tn_acc(const uint16_t* dY, int64_t ldy, const uint16_t* X, int64_t ldx, int M, int N, int K,
-                              float* dW, float* partial, int64_t partial_elems, hipStream_t s);
+                              float* dW, float* dbias, float* partial, int64_t partial_elems, hipStream_t s);
 int64_t gemm_tn_partial_elems(int M, int N, int K);
 
 // ---- LayerNorm / elementwise / loss (k_norm.hip, k_misc.hip) ----------------

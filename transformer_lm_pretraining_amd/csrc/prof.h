@@ -48,6 +48,7 @@ enum KernelClass {
     KC_TRANSPOSE = 22,
     KC_MEAN = 23,
     KC_BIAS_GELU_FWD = 24,
-    KC_OTHER = 25,
-    KC_COUNT = 26
+    KC_GEMM_NT_DGELU = 25, // gemm_kernel NT, output times GELU'(pre) epilogue
+    KC_OTHER = 26,
+    KC_COUNT = 27
 };

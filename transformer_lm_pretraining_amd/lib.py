@@ -82,7 +82,8 @@ _SIGS = {
     "gpt2k_bias_grad": (c_int32, [c_void_p] * 3 + [c_int64, c_int64, c_int32, c_void_p]),
     "gpt2k_gemm_nt": (c_int32, [c_void_p] * 5 + [c_int64] * 3 + [c_void_p]),
     "gpt2k_gemm_nt_gelu": (c_int32, [c_void_p] * 5 + [c_int64] * 3 + [c_void_p]),
-    "gpt2k_gemm_tn_acc": (c_int32, [c_void_p] * 4 + [c_int64] * 4 + [c_void_p]),
+    "gpt2k_gemm_nt_dgelu": (c_int32, [c_void_p] * 4 + [c_int64] * 3 + [c_void_p]),
+    "gpt2k_gemm_tn_acc": (c_int32, [c_void_p] * 5 + [c_int64] * 4 + [c_void_p]),
     "gpt2k_attention_fwd": (c_int32, [c_void_p] * 3 + [c_int32] * 4 + [c_void_p]),
     "gpt2k_attention_bwd": (c_int32, [c_void_p] * 6 + [c_int32] * 4 + [c_void_p]),
     "gpt2k_clip_adamw": (c_int32, [c_void_p] * 5 + [c_int64, c_int64, POINTER(AdamwArgs), c_void_p, c_void_p,
@@ -355,11 +356,21 @@ def gemm_nt_gelu(A, B, bias):
     return pre, g
 
 
-def gemm_tn_acc(dY, X, dW):
+def gemm_nt_dgelu(A, B, pre):
+    import torch
+    M, K = A.shape
+    N = B.shape[0]
+    out = torch.empty(M, N, dtype=torch.bfloat16, device=A.device)
+    check(load().gpt2k_gemm_nt_dgelu(_ptr(A), _ptr(B), _ptr(pre), _ptr(out), M, N, K, _stream()),
+          "gpt2k_gemm_nt_dgelu")
+    return out
+
+
+def gemm_tn_acc(dY, X, dW, db=None):
     M, N = dY.shape
     K = X.shape[1]
     s = _scratch(scratch_bytes(3, M, N, K), dY.device)
-    check(load().gpt2k_gemm_tn_acc(_ptr(dY), _ptr(X), _ptr(dW), _ptr(s), s.numel(), M, N, K, _stream()),
+    check(load().gpt2k_gemm_tn_acc(_ptr(dY), _ptr(X), _ptr(dW), _ptr(db), _ptr(s), s.numel(), M, N, K, _stream()),
           "gpt2k_gemm_tn_acc")
 
 
