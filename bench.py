@@ -27,6 +27,33 @@ PEAK_BF16 = 2.5e15     # MI355X dense bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12      # MI355X HBM3E, B/s
 METRIC = "GPT-2 124M train tokens/s on 1 MI355X (19x1024x9 accum); MFU vs bf16 peak"
 
+# HBM traffic per launch from two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE,
+# KiB per dispatch averaged over the gpt2_124m workload), each scaled by what the same
+# counter reads for a plain 1 GiB copy (read x2.000, write x1.000).  Valid only for the
+# kernel sources the counters were taken on: a changed source reports null.
+TRAFFIC_COUNTERS = {
+    ("gpt2_124m", "gemm_nt"): {
+        "sources": {"k_gemm.hip": "cb1bf18581aa82aacf192ed9e8c281ad36763494a39854c7c5218c087c1fcb9a",
+                    "common.h": "09cdf91791baa2de19911f14e9fb85ba680bbb96ba8302f6d0ef6c9caca3aaf4"},
+        "fetch_kib": 116826.06, "fetch_scale": 1.99994, "write_kib": 69599.57, "write_scale": 1.0,
+    },
+}
+
+
+def counted_traffic(workload, kernel):
+    """Bytes per launch from the counter runs, or None when none were taken for this
+    kernel and workload or its sources changed since."""
+    import hashlib
+    rec = TRAFFIC_COUNTERS.get((workload, kernel))
+    if rec is None:
+        return None
+    csrc = os.path.join(ROOT, "transformer_lm_pretraining_amd", "csrc")
+    for name, digest in rec["sources"].items():
+        with open(os.path.join(csrc, name), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != digest:
+                return None
+    return round((rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024)
+
 WORKLOADS = {
     # name: (L, H, C, V, Vp, Tmax, B, T, n_micro)
     "gpt2_124m": (12, 12, 768, 50257, 50304, 1024, 19, 1024, 9),
@@ -83,7 +110,21 @@ def main():
     ap.add_argument("--workload", default="gpt2_124m", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true", help="skip the per-kernel event timing")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        import torch
+        torch.cuda.set_device(0)
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 2, "copy_bytes_written": dst.numel() * 2,
+                          "launches": 5}), flush=True)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -161,17 +202,20 @@ def main():
 
     roof = None
     if dominant is not None:
+        traffic = counted_traffic(args.workload, dominant)
         ms, cnt, work = model.prof_read(dom_id)
         model.prof_enable(0)
         avg_ms = ms / cnt
         if dominant in lib.MFMA_CLASSES:
             achieved = work / (ms * 1e-3) / 1e12
             roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                    "frac": round(achieved / (PEAK_BF16 / 1e12), 4), "traffic": None}
+                    "frac": round(achieved / (PEAK_BF16 / 1e12), 4), "traffic": traffic,
+                    "traffic_unit": "bytes per launch"}
         else:
             achieved = work / (ms * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                    "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": None}
+                    "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": traffic,
+                    "traffic_unit": "bytes per launch"}
         roof.update({"kernel": dominant, "launches": cnt, "avg_launch_ms": round(avg_ms, 4),
                      "work_per_launch": work / cnt})
 
