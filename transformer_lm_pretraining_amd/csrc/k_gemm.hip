@@ -6,18 +6,18 @@
 //     contiguous along the reduction.  The input-gradient GEMMs use the
 //     transposed bf16 weight copy so they are NT products too;
 //   weight gradient ("TN"): dW[N,K] += sum_m dY[m,n] X[m,k], reduction over
-//     tokens, operands contiguous along the output dims.  Their tiles are
-//     transposed in registers (8x8 bf16 blocks) on the way into LDS, so the
-//     MFMA loop is identical for both.  The bias gradient (column sums of dY)
-//     is folded into the same pass: the workgroups of the first output column
-//     tile sum the dY tiles they load anyway.
-// Tiles: BM x BN per workgroup of WGM x WGN waves, K step 64, LDS double
-// buffered (one barrier per K step) with register prefetch of the next tile;
-// LDS rows padded to 72 bf16 (144 B) so the 16-byte fragment reads of 32
-// consecutive rows hit distinct banks.  Workgroups are renumbered so each of
-// the 8 XCDs (own L2 each) walks a contiguous run of the grouped tile order.
-// Weight-gradient GEMMs split the token reduction (uneven splits allowed) to
-// fill the 256 CUs; the fp32 partials are summed into dW by a second kernel.
+//     tokens, operands contiguous along the output dims.  Their MFMA fragments
+//     are read transposed out of LDS (ds_read_b64_tr_b16).  The bias gradient
+//     (column sums of dY) is folded into the same pass: the workgroups of the
+//     first output column tile sum the dY fragments they read anyway.
+// Large problems run 256x256 tiles (gemm_nt_pipe_kernel, gemm_tn_pipe_kernel):
+// operands go global -> LDS without register staging, several stages in
+// flight.  Small ones run the generic BM x BN kernel (gemm_kernel: register
+// prefetch, LDS double buffer, rows padded to 72 bf16).  Workgroups are
+// renumbered so each of the 8 XCDs (own L2 each) walks a contiguous run of the
+// grouped tile order.  Weight-gradient GEMMs split the token reduction (uneven
+// splits allowed) to fill the 256 CUs; the fp32 partials are summed into dW by
+// a second kernel.
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
@@ -270,32 +270,62 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Large NT tiles: 256x256 per workgroup, four 128x128 wave tiles.  Operands go
-// global -> LDS with global_load_lds_dwordx4 (no register staging): each wave
-// instruction fills 1 KB = 8 rows of 64 bf16.  Rows are unpadded (128 B) and
-// the 16-byte vector kv of row r sits at slot kv ^ ((r >> 1) & 7), which
-// makes the fragment reads of 16 consecutive rows hit 16 distinct bank
-// groups.  The MFMA takes B as its first operand, so a lane's accumulator
-// holds 4 consecutive output columns of one output row; the epilogue stages
-// the bf16 tile in LDS (16-byte chunks XOR-swizzled by row) and writes it
-// back in coalesced 16-byte row segments, applying bias / residual / GELU.
+// 256x256 tiles (one per workgroup of four waves) load their operands global ->
+// LDS with global_load_lds_dwordx4: each wave instruction fills 1 KB of LDS at
+// M0 + 16 * lane, so the swizzle of a tile is chosen by which global vector each
+// lane fetches.
 constexpr int BIG = 256;
-constexpr int BIG_STAGE = 2 * BIG * BK;  // A and B tiles of one stage, bf16 elements
 
 __device__ __forceinline__ void lds_dma16(const uint16_t* src, uint16_t* dst_wave_base) {
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                      (__attribute__((address_space(3))) void*)dst_wave_base, 16, 0, 0);
 }
 
-__device__ __forceinline__ int big_slot(int row, int kv) { return row * BK + ((kv ^ ((row >> 1) & 7)) << 3); }
+// ---------------------------------------------------------------------------
+// Pipelined NT tiles: 256x256 per workgroup, four 128x128 wave tiles, the
+// reduction walked in stages of 32.  NS stage buffers live in LDS and NS-1 of
+// them are in flight while one is consumed, so each CU keeps 96-128 KB of
+// loads outstanding (the loaded memory latency is about 1-2 us, the MFMA time
+// of a stage about 0.4 us).  Each wave instruction of
+// global_load_lds_dwordx4 fills 1 KB = 16 rows of 32 bf16; the 16-byte
+// vector c of row r sits at slot c ^ ((r >> 2) & 3) so the fragment reads of
+// 16 consecutive rows hit 16 distinct 16-byte bank groups.  Waits count
+// outstanding loads (vmcnt) per stage, and the one barrier per stage sits
+// between the two halves of the last MFMA group, with the next stage's first
+// fragments read right after it.  The bias is loaded into the accumulators
+// before the first MFMA.  The MFMA takes B as its first operand, so a lane's
+// accumulator holds 4 consecutive output columns of one output row.
+#ifndef NT_STAGES
+#define NT_STAGES 4
+#endif
+constexpr int PBK = 32;                  // reduction depth of one stage
+constexpr int PSTAGE = 2 * BIG * PBK;    // A and B tiles of one stage, bf16 elements (32 KB)
 
-__device__ __forceinline__ const bf16x8& big_frag(const uint16_t* tile, int row, int kv) {
-    return *(const bf16x8*)(tile + big_slot(row, kv));
+// Read one accumulator element out of its AGPR where it is needed, so the
+// epilogue never asks for all 256 accumulators in VGPRs at once (which makes
+// the register allocator spill them around the main loop).
+__device__ __forceinline__ float acc_read(float x) {
+    float r;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
+    return r;
 }
 
-template <int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_nt_big_kernel(GemmParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BIG_STAGE];
+// Wait until at most n stage groups (8 loads per wave each) are still in flight.
+__device__ __forceinline__ void wait_stage_groups(int n) {
+    // s_waitcnt immediate: vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt[5:4] at [15:14]
+    switch (n) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        case 1: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0x4F70); break;
+        case 3: __builtin_amdgcn_s_waitcnt(0x4F78); break;
+        default: __builtin_amdgcn_s_waitcnt(0x8F70); break;
+    }
+}
+
+template <int EPI, int NS>
+__global__ __launch_bounds__(256, 1) void gemm_nt_pipe_kernel(GemmParams p) {
+    static_assert(NS >= 4 && NS <= 5, "the epilogue reuses 128 KB of stage buffers");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NS * PSTAGE];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
     const int wm = wave >> 1, wn = wave & 1;
 
@@ -307,93 +337,138 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_big_kernel(GemmParams p) {
     const int gsize = min(p.tiles_m - first_m, GROUP_M);
     const int m0 = (first_m + (pid % in_group) % gsize) * BIG;
     const int n0 = ((pid % in_group) / gsize) * BIG;
-    const int nk = p.nk_total;
+    const int nk = p.nk_total * (BK / PBK);
 
-    // Lane source of this wave's chunk i (rows 64*wave + 8*i + lane/8): the row is
-    // clamped into range (rows past M / N load valid memory whose products are
-    // never stored) and the vector slot is un-swizzled.  Offsets are 32-bit
+    // Lane q of load instruction i covers row 64*wave + 16*i + q/4 at physical
+    // slot q&3, i.e. logical vector (q&3) ^ ((q>>4)&3).  Rows past M / N are
+    // clamped (their products are never stored).  Offsets are 32-bit elements
     // (the host checks M*lda and N*ldb < 2^31).
-    const int lrow = lane >> 3, pv = lane & 7;
-    const int kv_even = (pv ^ (lrow >> 1)) << 3;        // chunks i even: (row >> 1) & 7 == lrow >> 1
-    const int kv_odd = (pv ^ ((lrow >> 1) + 4)) << 3;   // chunks i odd: 4 + lrow >> 1
-    const int rowA = m0 + wave * 64 + lrow, rowB = n0 + wave * 64 + lrow;
-    const int lda = (int)p.lda, ldb = (int)p.ldb;
-    auto issue = [&](int stage, int k0) {
-        uint16_t* sa = smem + stage * BIG_STAGE;
-        uint16_t* sb = sa + BIG * BK;
+    const int lvec = ((lane & 3) ^ ((lane >> 4) & 3)) << 3;
+    uint32_t offA[4], offB[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int kv = (i & 1) ? kv_odd : kv_even;
-            lds_dma16(p.A + (uint32_t)(min(rowA + 8 * i, p.M - 1) * lda + k0 + kv), sa + (wave * 8 + i) * 512);
-        }
+    for (int i = 0; i < 4; ++i) {
+        offA[i] = (uint32_t)min(m0 + wave * 64 + 16 * i + (lane >> 2), p.M - 1) * (uint32_t)p.lda + lvec;
+        offB[i] = (uint32_t)min(n0 + wave * 64 + 16 * i + (lane >> 2), p.N - 1) * (uint32_t)p.ldb + lvec;
+    }
+    auto issue = [&](int t) {
+        uint16_t* sa = smem + (t % NS) * PSTAGE;
+        uint16_t* sb = sa + BIG * PBK;
+        const uint32_t k0 = (uint32_t)t * PBK;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int kv = (i & 1) ? kv_odd : kv_even;
-            lds_dma16(p.B + (uint32_t)(min(rowB + 8 * i, p.N - 1) * ldb + k0 + kv), sb + (wave * 8 + i) * 512);
-        }
+        for (int i = 0; i < 4; ++i) lds_dma16(p.A + (offA[i] + k0), sa + (wave * 64 + 16 * i) * PBK);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_dma16(p.B + (offB[i] + k0), sb + (wave * 64 + 16 * i) * PBK);
     };
 
+    // prologue: the first NS-1 stages in flight (nk >= 1: the host requires K >= 64)
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t)
+        if (t < nk) issue(t);
+    __builtin_amdgcn_sched_barrier(0);
+    // bias of this lane's 16 column groups (zero past N; N % 8 == 0 keeps a group whole)
+    float4 b4[4][4];
+    if ((EPI == EPI_BF16 || EPI == EPI_GELU) && p.bias != nullptr) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg)
+                b4[j][rg] = *(const float4*)(p.bias + min(n0 + wn * 128 + j * 32 + 8 * rg + 4 * g, p.N - 4));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const bool in = n0 + wn * 128 + j * 32 + 8 * rg + 4 * g < p.N;
+                b4[j][rg].x = in ? b4[j][rg].x : 0.f;
+                b4[j][rg].y = in ? b4[j][rg].y : 0.f;
+                b4[j][rg].z = in ? b4[j][rg].z : 0.f;
+                b4[j][rg].w = in ? b4[j][rg].w : 0.f;
+            }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) b4[j][rg] = float4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // accumulators start at the bias of their columns.
+    // acc[i][j][4*rg + e] is C[m0 + wm*128 + i*32 + (lane&31)][n0 + wn*128 + j*32 + 8*rg + 4*g + e].
     floatx16 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    issue(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
+            for (int rg = 0; rg < 4; ++rg) {
+                acc[i][j][4 * rg + 0] = b4[j][rg].x;
+                acc[i][j][4 * rg + 1] = b4[j][rg].y;
+                acc[i][j][4 * rg + 2] = b4[j][rg].z;
+                acc[i][j][4 * rg + 3] = b4[j][rg].w;
+            }
+    wait_stage_groups(min(NS - 1, nk) - 1);
     __syncthreads();
+
+    // Fragment rows are fixed per lane; the two 16-deep halves of a stage are
+    // vectors g and 2+g, swizzled by the row's (r>>2)&3 (rows are 32-aligned + lane&31).
     const int fr = lane & 31;
-    // fragment rows are fixed per lane: precompute the LDS element offsets of the
-    // 4 A and 4 B fragment rows (swizzle term included) for both K halves g
-    const int ra = wm * 128 + fr, rb = wn * 128 + fr;
+    const int cv0 = (g ^ ((fr >> 2) & 3)) << 3, cv1 = cv0 ^ 16;
+    const int ra = (wm * 128 + fr) * PBK, rb = (wn * 128 + fr) * PBK;
     bf16x8 af[2][4], bfr[2][4];
-    auto load_frags = [&](const uint16_t* sa, const uint16_t* sb, int kk, int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[buf][i] = big_frag(sa, ra + i * 32, 2 * kk + g);
+    for (int i = 0; i < 4; ++i) af[0][i] = *(const bf16x8*)(smem + ra + i * 32 * PBK + cv0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bfr[buf][j] = big_frag(sb, rb + j * 32, 2 * kk + g);
-    };
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) issue(cur ^ 1, (kt + 1) * BK);
-        const uint16_t* sa = smem + cur * BIG_STAGE;
-        const uint16_t* sb = sa + BIG * BK;
-        load_frags(sa, sb, 0, 0);
+    for (int j = 0; j < 4; ++j) bfr[0][j] = *(const bf16x8*)(smem + BIG * PBK + rb + j * 32 * PBK + cv0);
+    int s = 0;
+    do {
+        const uint16_t* sa = smem + (s % NS) * PSTAGE;
+        const uint16_t* sb = sa + BIG * PBK;
+        // first half of the stage (fragments [0]); the second half's are read meanwhile
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(bfr[0][j], af[0][i], acc[i][j]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int cb = kk & 1, nb = cb ^ 1;
-            // next step's A fragments (4 reads), then half of this step's MFMAs
-            if (kk + 1 < BK / 16) {
+        for (int i = 0; i < 4; ++i) af[1][i] = *(const bf16x8*)(sa + ra + i * 32 * PBK + cv1);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) af[nb][i] = big_frag(sa, ra + i * 32, 2 * (kk + 1) + g);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < 4; ++j) bfr[1][j] = *(const bf16x8*)(sb + rb + j * 32 * PBK + cv1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+        for (int i = 2; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(bfr[cb][j], af[cb][i], acc[i][j]);
-            __builtin_amdgcn_sched_barrier(0);
-            // next step's B fragments, then the other half
-            if (kk + 1 < BK / 16) {
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(bfr[0][j], af[0][i], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+        // second half (fragments [1])
 #pragma unroll
-                for (int j = 0; j < 4; ++j) bfr[nb][j] = big_frag(sb, rb + j * 32, 2 * (kk + 1) + g);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int i = 2; i < 4; ++i)
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(bfr[1][j], af[1][i], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 < nk) {
+            // stage s+1 has landed once only the stages issued after it remain in flight
+            wait_stage_groups(min(s + NS - 2, nk - 1) - (s + 1));
+            __syncthreads();
+            // every wave is past stage s-1, whose buffer takes stage s+NS-1
+            if (s + NS - 1 < nk) issue(s + NS - 1);
+            const uint16_t* na = smem + ((s + 1) % NS) * PSTAGE;
+            const uint16_t* nb = na + BIG * PBK;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(bfr[cb][j], af[cb][i], acc[i][j]);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < 4; ++i) af[0][i] = *(const bf16x8*)(na + ra + i * 32 * PBK + cv0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bfr[0][j] = *(const bf16x8*)(nb + rb + j * 32 * PBK + cv0);
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 2; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(bfr[1][j], af[1][i], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+    } while (++s < nk);
+    // all fragment reads done: the stage buffers become the output tile (the
+    // barrier also covers the MFMA -> accumulator-read latency)
+    __syncthreads();
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
-    // stage 1: acc (+bias) -> bf16 tile [256][256] in LDS.  acc[i][j][4*rg + e] is
-    // C[m0 + wm*128 + i*32 + (lane&31)][n0 + wn*128 + j*32 + 8*rg + 4*g + e].
+    // stage 1: acc -> bf16 tile [256][256] in LDS.
     uint16_t* so = smem;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -403,17 +478,10 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_big_kernel(GemmParams p) {
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 const int col = wn * 128 + j * 32 + 8 * rg + 4 * g;
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * rg + e];
-                if constexpr (EPI == EPI_BF16 || EPI == EPI_GELU) {
-                    if (p.bias && n0 + col < p.N) {
-                        const float4 b4 = *(const float4*)(p.bias + n0 + col);
-                        v[0] += b4.x; v[1] += b4.y; v[2] += b4.z; v[3] += b4.w;
-                    }
-                }
                 const int chunk = (col >> 3) ^ (row & 31);
-                *(u32x2*)(so + row * BIG + chunk * 8 + (col & 7)) = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+                *(u32x2*)(so + row * BIG + chunk * 8 + (col & 7)) =
+                    u32x2{pack_bf2(acc_read(acc[i][j][4 * rg]), acc_read(acc[i][j][4 * rg + 1])),
+                          pack_bf2(acc_read(acc[i][j][4 * rg + 2]), acc_read(acc[i][j][4 * rg + 3]))};
             }
     }
     __syncthreads();
@@ -450,19 +518,46 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_big_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Large TN tiles (weight gradients): dW[n][k] (+)= sum_m dY[m][n] X[m][k] over
-// one split's token range, 256x256 output tile, four 128x128 wave tiles.  Both
-// operands are stored token-major, so each thread loads an 8 (tokens) x 8
-// (features) block of each (8 row vectors), transposes it in registers and
-// writes 8 token vectors into the swizzled LDS layout used by the NT kernel.
-// Loads are issued one K step ahead into registers (two LDS stages).  The
-// workgroups of output column tile 0 also sum the dY blocks they transpose
-// (the bias gradient, added atomically).  Lane l of wave tile (wm, wn) holds
-// output rows wm*128 + 32i + (l&31) and 4 consecutive columns per register
-// group, written as float4.
-template <int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_tn_big_kernel(GemmParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BIG_STAGE];
+// Pipelined TN tiles (weight gradients): dW[r][c] (+)= sum_t dY[t][r] X[t][c]
+// over one split's token range, 256x256 output tile, four 128x128 wave tiles.
+// Both operands are token-major, so a stage holds 32 tokens x 256 features of
+// each, loaded straight into LDS (global_load_lds_dwordx4: 1 KB = 2 token
+// rows of 512 B per wave instruction) with the 16-byte vector v of row t at
+// slot v ^ ((t & 7) << 2).  The MFMA fragments are the transposes of those
+// tiles, read with ds_read_b64_tr_b16 (8 consecutive tokens of one feature
+// per lane); the XOR spreads the 8 token rows one read touches over the banks.
+// Pipeline, waits and barrier placement are those of the NT kernel (the loads
+// are issued through inline asm, see lds_dma16_asm).  The
+// workgroups of output column tile 0 also sum the dY fragments they read (the
+// bias gradient).  The fp32 epilogue goes through a per-wave LDS buffer so
+// each row segment is written (or read-modified-written) in 512-byte runs.
+
+// LDS element offset of (token t, feature f) within a 32 x 256 stage tile.
+__device__ __forceinline__ int tn_off(int t, int f) { return t * BIG + (((f >> 3) ^ ((t & 7) << 2)) << 3) + (f & 7); }
+
+typedef short tn_v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 tn_frag(const uint16_t* p) {
+    // two transposed 4-element reads 8 token rows apart: tokens 16ks + 4g + 0..3, then + 8
+    const tn_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tn_v4s*)p);
+    const tn_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tn_v4s*)(p + 8 * BIG));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// lds_dma16 written as inline asm.  With the builtin, the compiler treats every
+// in-flight load-to-LDS as possibly aliasing a ds_read_b64_tr_b16 (which carries
+// no memory operand) and drains all outstanding loads before each one, which
+// leaves a single stage in flight.  Completion of these loads is tracked by the
+// explicit vmcnt waits and barriers around the stage buffers instead.
+__device__ __forceinline__ void lds_dma16_asm(const uint16_t* src, uint16_t* dst_wave_base) {
+    const uint32_t lds =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)dst_wave_base);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+}
+
+template <int EPI, int NS>
+__global__ __launch_bounds__(256, 1) void gemm_tn_pipe_kernel(GemmParams p) {
+    static_assert(NS >= 2 && NS <= 5, "stage count");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NS * PSTAGE];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
     const int wm = wave >> 1, wn = wave & 1;
 
@@ -477,46 +572,42 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_big_kernel(GemmParams p) {
     const int gsize = min(p.tiles_m - first_m, GROUP_M);
     const int tm = first_m + (pid % in_group) % gsize;
     const int tn = (pid % in_group) / gsize;
-    const int m0 = tm * BIG, n0 = tn * BIG;
-    const int q = p.nk_total / p.splits, rr = p.nk_total % p.splits;
-    const int nk = q + (split < rr ? 1 : 0);
-    const int kbeg = (split * q + min(split, rr)) * BK;
-    const bool sum_rows = p.dbias != nullptr && tn == 0;
+    const int m0 = tm * BIG, n0 = tn * BIG;  // dY feature (output row) and X feature (output column) origins
+    const int steps = p.nk_total * (BK / PBK);
+    const int q = steps / p.splits, rr = steps % p.splits;
+    const int nk = q + (split < rr ? 1 : 0);                 // >= 1: the host keeps splits <= steps
+    const int tok0 = (split * q + min(split, rr)) * PBK;
+    const bool sum_rows = p.dbias != nullptr && tn == 0 && wn == 0;
 
-    // thread t owns feature chunk fc = t >> 3 (8 features) and token chunk tc = t & 7
-    // (8 tokens) of each 256 x 64 operand tile
-    const int fc = tid >> 3, tc = tid & 7;
-    const int fa = min(m0 + fc * 8, p.M - 8), fb = min(n0 + fc * 8, p.N - 8);  // clamped (M, N % 8 == 0)
-    u32x4 va[8], vb[8];
-    float bs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    auto gload = [&](int k0) {
-        const int tok = kbeg + k0 + tc * 8;
+    // Load instruction i of this wave covers token rows 8*wave + 2*i + (lane>>5) of
+    // the stage, physical vector lane&31, i.e. logical vector (lane&31) ^ ((row&7)<<2).
+    // Features past M / N are clamped (their products are never stored).
+    uint32_t offA[4], offB[4];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) va[r] = *(const u32x4*)(p.A + (int64_t)(tok + r) * p.lda + fa);
+    for (int i = 0; i < 4; ++i) {
+        const int row = 8 * wave + 2 * i + g;
+        const int lv = (lane & 31) ^ ((row & 7) << 2);
+        offA[i] = (uint32_t)(tok0 + row) * (uint32_t)p.lda + (uint32_t)min(m0 + lv * 8, p.M - 8);
+        offB[i] = (uint32_t)(tok0 + row) * (uint32_t)p.ldb + (uint32_t)min(n0 + lv * 8, p.N - 8);
+    }
+    const uint32_t stepA = (uint32_t)PBK * (uint32_t)p.lda, stepB = (uint32_t)PBK * (uint32_t)p.ldb;
+    auto issue = [&](int t) {
+        uint16_t* sa = smem + (t % NS) * PSTAGE;
+        uint16_t* sb = sa + PBK * BIG;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) vb[r] = *(const u32x4*)(p.B + (int64_t)(tok + r) * p.ldb + fb);
-    };
-    auto lstore = [&](int stage) {
-        uint16_t* sa = smem + stage * BIG_STAGE;
-        uint16_t* sb = sa + BIG * BK;
-        u32x4 w[8];
-        transpose8x8(va, w);
+        for (int i = 0; i < 4; ++i)
+            lds_dma16_asm(p.A + (offA[i] + (uint32_t)t * stepA), sa + (8 * wave + 2 * i) * BIG);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) *(u32x4*)(sa + big_slot(fc * 8 + c, tc)) = w[c];
-        if (sum_rows) {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                float t = 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) t += bflo(w[c][e]) + bfhi(w[c][e]);
-                bs[c] += t;
-            }
-        }
-        transpose8x8(vb, w);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) *(u32x4*)(sb + big_slot(fc * 8 + c, tc)) = w[c];
+        for (int i = 0; i < 4; ++i)
+            lds_dma16_asm(p.B + (offB[i] + (uint32_t)t * stepB), sb + (8 * wave + 2 * i) * BIG);
     };
 
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t)
+        if (t < nk) issue(t);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // acc[i][j][4*rg + e] is dW[m0 + wm*128 + i*32 + (lane&31)][n0 + wn*128 + j*32 + 8*rg + 4*g + e]
     floatx16 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -524,91 +615,121 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_big_kernel(GemmParams p) {
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    if (nk > 0) {
-        gload(0);
-        lstore(0);
-        if (nk > 1) gload(BK);
-    }
+    float bsum[4] = {0.f, 0.f, 0.f, 0.f};
+    wait_stage_groups(min(NS - 1, nk) - 1);
     __syncthreads();
-    const int fr = lane & 31;
-    const int ra = wm * 128 + fr, rb = wn * 128 + fr;
-    bf16x8 af[2][4], bfr[2][4];
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const uint16_t* sa = smem + cur * BIG_STAGE;
-        const uint16_t* sb = sa + BIG * BK;
+
+    // per-lane fragment addresses within a stage tile (token row 4g + (lane&15)/4,
+    // features col0 + 16*((lane>>4)&1) + 4*(lane&3), col0 = 32-column subtile)
+    int fa[4], fb[4];
+    {
+        const int t = 4 * g + ((lane & 15) >> 2);
+        const int f = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[0][i] = big_frag(sa, ra + i * 32, g);
+        for (int i = 0; i < 4; ++i) {
+            fa[i] = tn_off(t, wm * 128 + i * 32 + f);
+            fb[i] = PBK * BIG + tn_off(t, wn * 128 + i * 32 + f);
+        }
+    }
+    bf16x8 dyf[2][4], xf[2][4];
+    auto read_frags = [&](const uint16_t* st, int ks, int b) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bfr[0][j] = big_frag(sb, rb + j * 32, g);
+        for (int i = 0; i < 4; ++i) dyf[b][i] = tn_frag(st + fa[i] + ks * 16 * BIG);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xf[b][j] = tn_frag(st + fb[j] + ks * 16 * BIG);
+    };
+    auto add_bias = [&](int b) {
+        if (sum_rows) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x4 w = __builtin_bit_cast(u32x4, dyf[b][i]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bsum[i] += bflo(w[e]) + bfhi(w[e]);
+            }
+        }
+    };
+    read_frags(smem, 0, 0);
+    int s = 0;
+    do {
+        const uint16_t* st = smem + (s % NS) * PSTAGE;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(xf[0][j], dyf[0][i], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(st, 1, 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int cb = kk & 1, nb = cb ^ 1;
-            if (kk + 1 < BK / 16) {
+        for (int i = 2; i < 4; ++i)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) af[nb][i] = big_frag(sa, ra + i * 32, 2 * (kk + 1) + g);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(xf[0][j], dyf[0][i], acc[i][j]);
+        add_bias(0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(bfr[cb][j], af[cb][i], acc[i][j]);
-            __builtin_amdgcn_sched_barrier(0);
-            if (kk + 1 < BK / 16) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) bfr[nb][j] = big_frag(sb, rb + j * 32, 2 * (kk + 1) + g);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 2; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(bfr[cb][j], af[cb][i], acc[i][j]);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(xf[1][j], dyf[1][i], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 < nk) {
+            wait_stage_groups(min(s + NS - 2, nk - 1) - (s + 1));
+            __syncthreads();
+            if (s + NS - 1 < nk) issue(s + NS - 1);
+            read_frags(smem + ((s + 1) % NS) * PSTAGE, 0, 0);
         }
-        // every wave is done with the other stage since the previous barrier: fill it
-        // with K step kt+1 (in registers) and start the loads of step kt+2
-        if (kt + 1 < nk) {
-            lstore(cur ^ 1);
-            if (kt + 2 < nk) gload((kt + 2) * BK);
-        }
-        __syncthreads();
-    }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 2; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(xf[1][j], dyf[1][i], acc[i][j]);
+        add_bias(1);
+        __builtin_amdgcn_sched_barrier(0);
+    } while (++s < nk);
+    __syncthreads();
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
     if (sum_rows) {
-        // sum the 8 token chunks of each feature row, add to the bias gradient
-        float* red = (float*)smem;
+        // the two lane halves hold different tokens of the same feature rows
 #pragma unroll
-        for (int c = 0; c < 8; ++c) red[tc * BIG + fc * 8 + c] = bs[c];
-        __syncthreads();
-        float t = 0.f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) t += red[k * BIG + tid];
-        if (m0 + tid < p.M) unsafeAtomicAdd(p.dbias + m0 + tid, t);
+        for (int i = 0; i < 4; ++i) {
+            const float t = bsum[i] + __shfl_xor(bsum[i], 32, WAVE);
+            const int row = m0 + wm * 128 + i * 32 + (lane & 31);
+            if (g == 0 && row < p.M) unsafeAtomicAdd(p.dbias + row, t);
+        }
     }
 
+    // Epilogue through a per-wave 32 x 128 fp32 buffer (16 KB), one 32-row group i
+    // at a time: 16-byte vector v of buffer row r sits at slot v ^ r.
+    float* buf = (float*)smem + wave * (32 * 128);
+    const int fr = lane & 31;
+    float* outp = EPI == EPI_F32_ACC ? p.outf : p.outf + split * p.split_stride;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int row = m0 + wm * 128 + i * 32 + fr;
-        if (row >= p.M) continue;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-                const int col = n0 + wn * 128 + j * 32 + 8 * rg + 4 * g;
-                if (col >= p.N) continue;
-                float4 v = make_float4(acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2],
-                                       acc[i][j][4 * rg + 3]);
+                const int v = 8 * j + 2 * rg + g;  // 16-byte vector index within the 128-column row
+                *(float4*)(buf + fr * 128 + ((v ^ fr) << 2)) =
+                    make_float4(acc_read(acc[i][j][4 * rg]), acc_read(acc[i][j][4 * rg + 1]),
+                                acc_read(acc[i][j][4 * rg + 2]), acc_read(acc[i][j][4 * rg + 3]));
+            }
+        // read back row-contiguous: lane covers vector lane&31 of rows 2*it + g
+#pragma unroll 4
+        for (int it = 0; it < 16; ++it) {
+            const int r = 2 * it + g, v = lane & 31;
+            const float4 a = *(const float4*)(buf + r * 128 + ((v ^ r) << 2));
+            const int row = m0 + wm * 128 + i * 32 + r, col = n0 + wn * 128 + v * 4;
+            if (row < p.M && col < p.N) {
+                float4* o = (float4*)(outp + (int64_t)row * p.ldf + col);
                 if constexpr (EPI == EPI_F32_ACC) {
-                    float4* o = (float4*)(p.outf + (int64_t)row * p.ldf + col);
-                    float4 a = *o;
-                    a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
-                    *o = a;
+                    float4 c = *o;
+                    c.x += a.x; c.y += a.y; c.z += a.z; c.w += a.w;
+                    *o = c;
                 } else {
-                    *(float4*)(p.outf + split * p.split_stride + (int64_t)row * p.ldf + col) = v;
+                    *o = a;
                 }
             }
+        }
     }
 }
 
@@ -654,7 +775,8 @@ hipError_t run_nt(GemmParams p, hipStream_t s) {
         p.tiles_n = (int)cdiv(p.N, BIG);
         const double work = 2.0 * p.M * p.N * (double)p.nk_total * BK;
         PROF_LAUNCH(gemm_class(false, EPI), work, s,
-                    hipLaunchKernelGGL(gemm_nt_big_kernel<EPI>, dim3(p.tiles_m * p.tiles_n), dim3(256), 0, s, p));
+                    hipLaunchKernelGGL((gemm_nt_pipe_kernel<EPI, NT_STAGES>), dim3(p.tiles_m * p.tiles_n), dim3(256),
+                                       0, s, p));
         return hipGetLastError();
     }
     return run<128, 128, 2, 2, false, false, EPI>(p, s);
@@ -666,8 +788,8 @@ hipError_t run_tn_big(GemmParams p, hipStream_t s) {
     p.tiles_n = (int)cdiv(p.N, BIG);
     const double work = 2.0 * p.M * p.N * (double)p.nk_total * BK;
     PROF_LAUNCH(gemm_class(true, EPI), work, s,
-                hipLaunchKernelGGL(gemm_tn_big_kernel<EPI>, dim3(p.tiles_m * p.tiles_n * p.splits), dim3(256), 0,
-                                   s, p));
+                hipLaunchKernelGGL((gemm_tn_pipe_kernel<EPI, NT_STAGES>), dim3(p.tiles_m * p.tiles_n * p.splits),
+                                   dim3(256), 0, s, p));
     return hipGetLastError();
 }
 
@@ -677,9 +799,9 @@ struct TnPlan {
     int splits;
     bool big;  // 256x256 tiles
 };
-TnPlan tn_plan(int M, int N, int K) {
+TnPlan tn_plan(int M, int N, int K, bool pipe_ok = true) {
     const int nk = M / BK;
-    const bool big = (int64_t)cdiv(N, 256) * cdiv(K, 256) >= 8;
+    const bool big = pipe_ok && (int64_t)cdiv(N, 256) * cdiv(K, 256) >= 8;
     const int64_t tiles = big ? cdiv(N, 256) * cdiv(K, 256) : cdiv(N, 128) * cdiv(K, 128);
     if (tiles >= NUM_CU) return {1, big};
     int best = 1;
@@ -731,7 +853,9 @@ int64_t gemm_tn_partial_elems(int M, int N, int K) {
 hipError_t launch_gemm_tn_acc(const uint16_t* dY, int64_t ldy, const uint16_t* X, int64_t ldx, int M, int N, int K,
                               float* dW, float* dbias, float* partial, int64_t partial_elems, hipStream_t s) {
     // output rows = N (features of dY), output cols = K (features of X), reduction = M tokens
-    TnPlan t = tn_plan(M, N, K);
+    // the pipelined kernel addresses operands with 32-bit element offsets and 16-byte vectors
+    const bool pipe_ok = ldy % 8 == 0 && ldx % 8 == 0 && (int64_t)M * ldy < (1ll << 31) && (int64_t)M * ldx < (1ll << 31);
+    TnPlan t = tn_plan(M, N, K, pipe_ok);
     if (t.splits > 1 && (partial == nullptr || partial_elems < (int64_t)t.splits * N * K)) t.splits = 1;
     GemmParams p{};
     p.A = dY; p.B = X; p.lda = ldy; p.ldb = ldx; p.M = N; p.N = K; p.nk_total = M / BK; p.splits = t.splits;
