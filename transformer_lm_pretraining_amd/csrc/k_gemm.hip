@@ -30,7 +30,8 @@ constexpr int GROUP_M = 8;
 constexpr int NUM_XCD = 8;
 constexpr int NUM_CU = 256;
 
-enum Epi { EPI_BF16 = 0, EPI_GELU = 1, EPI_DGELU = 2, EPI_F32_ACC = 3, EPI_F32_STORE = 4 };
+// EPI_BF16R: bias + residual (large-tile kernel only; the generic kernel handles p.res under EPI_BF16)
+enum Epi { EPI_BF16 = 0, EPI_GELU = 1, EPI_DGELU = 2, EPI_F32_ACC = 3, EPI_F32_STORE = 4, EPI_BF16R = 5 };
 
 struct GemmParams {
     const uint16_t* A;
@@ -41,7 +42,7 @@ struct GemmParams {
     int splits;
     int tiles_m, tiles_n;
     const float* bias;
-    const uint16_t* res;   // residual (EPI_BF16) or pre-activation (EPI_DGELU)
+    const uint16_t* res;   // residual (EPI_BF16 / EPI_BF16R) or pre-activation (EPI_DGELU)
     int64_t ldr;
     uint16_t* out;
     uint16_t* out2;
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_pipe_kernel(GemmParams p) {
     __builtin_amdgcn_sched_barrier(0);
     // bias of this lane's 16 column groups (zero past N; N % 8 == 0 keeps a group whole)
     float4 b4[4][4];
-    if ((EPI == EPI_BF16 || EPI == EPI_GELU) && p.bias != nullptr) {
+    if ((EPI == EPI_BF16 || EPI == EPI_BF16R || EPI == EPI_GELU) && p.bias != nullptr) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -468,6 +469,20 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_pipe_kernel(GemmParams p) {
     __syncthreads();
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
+    // The epilogue's second input (residual, or GELU's pre-activation) is read
+    // for the whole tile now, so its latency overlaps the staging below.  Thread
+    // tid covers 16-byte chunk (tid & 31) of rows 8*it + tid/32, it = 0..31.
+    constexpr int EIT = BIG * BIG / 8 / 256;
+    constexpr bool HAS_IN = EPI == EPI_DGELU || EPI == EPI_BF16R;
+    u32x4 pin[HAS_IN ? EIT : 1];
+    if constexpr (HAS_IN) {
+#pragma unroll
+        for (int it = 0; it < EIT; ++it) {
+            const int grow = m0 + it * 8 + (tid >> 5), gcol = n0 + (tid & 31) * 8;
+            pin[it] = (grow < p.M && gcol < p.N) ? *(const u32x4*)(p.res + (int64_t)grow * p.ldr + gcol) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
     // stage 1: acc -> bf16 tile [256][256] in LDS.
     uint16_t* so = smem;
 #pragma unroll
@@ -486,20 +501,18 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_pipe_kernel(GemmParams p) {
     }
     __syncthreads();
     // stage 2: coalesced 16-byte row segments
-#pragma unroll 4
-    for (int it = 0; it < BIG * BIG / 8 / 256; ++it) {
-        const int idx = it * 256 + tid;
-        const int row = idx >> 5, chunk = idx & 31;
+    auto out_chunk = [&](int it) {
+        const int row = it * 8 + (tid >> 5), chunk = tid & 31;
         const int grow = m0 + row, gcol = n0 + chunk * 8;
-        if (grow >= p.M || gcol >= p.N) continue;
+        if (grow >= p.M || gcol >= p.N) return;
         u32x4 w = *(const u32x4*)(so + row * BIG + ((chunk ^ (row & 31)) << 3));
         const int64_t o = (int64_t)grow * p.ldo + gcol;
         if constexpr (EPI == EPI_BF16) {
-            if (p.res) {
-                const u32x4 r = *(const u32x4*)(p.res + (int64_t)grow * p.ldr + gcol);
+            *(u32x4*)(p.out + o) = w;
+        } else if constexpr (EPI == EPI_BF16R) {
+            const u32x4 r = pin[it];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = pack_bf2(bflo(w[e]) + bflo(r[e]), bfhi(w[e]) + bfhi(r[e]));
-            }
+            for (int e = 0; e < 4; ++e) w[e] = pack_bf2(bflo(w[e]) + bflo(r[e]), bfhi(w[e]) + bfhi(r[e]));
             *(u32x4*)(p.out + o) = w;
         } else if constexpr (EPI == EPI_GELU) {
             u32x4 gv;
@@ -508,12 +521,19 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_pipe_kernel(GemmParams p) {
             *(u32x4*)(p.out + o) = w;
             *(u32x4*)(p.out2 + o) = gv;
         } else {  // EPI_DGELU
-            const u32x4 pr = *(const u32x4*)(p.res + (int64_t)grow * p.ldr + gcol);
+            const u32x4 pr = pin[it];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 w[e] = pack_bf2(bflo(w[e]) * gelu_grad_f(bflo(pr[e])), bfhi(w[e]) * gelu_grad_f(bfhi(pr[e])));
             *(u32x4*)(p.out + o) = w;
         }
+    };
+    if constexpr (HAS_IN) {
+#pragma unroll
+        for (int it = 0; it < EIT; ++it) out_chunk(it);
+    } else {
+#pragma unroll 4
+        for (int it = 0; it < EIT; ++it) out_chunk(it);
     }
 }
 
@@ -774,9 +794,14 @@ hipError_t run_nt(GemmParams p, hipStream_t s) {
         p.tiles_m = (int)cdiv(p.M, BIG);
         p.tiles_n = (int)cdiv(p.N, BIG);
         const double work = 2.0 * p.M * p.N * (double)p.nk_total * BK;
-        PROF_LAUNCH(gemm_class(false, EPI), work, s,
-                    hipLaunchKernelGGL((gemm_nt_pipe_kernel<EPI, NT_STAGES>), dim3(p.tiles_m * p.tiles_n), dim3(256),
-                                       0, s, p));
+        if (EPI == EPI_BF16 && p.res != nullptr)
+            PROF_LAUNCH(gemm_class(false, EPI), work, s,
+                        hipLaunchKernelGGL((gemm_nt_pipe_kernel<EPI_BF16R, NT_STAGES>), dim3(p.tiles_m * p.tiles_n),
+                                           dim3(256), 0, s, p));
+        else
+            PROF_LAUNCH(gemm_class(false, EPI), work, s,
+                        hipLaunchKernelGGL((gemm_nt_pipe_kernel<EPI, NT_STAGES>), dim3(p.tiles_m * p.tiles_n),
+                                           dim3(256), 0, s, p));
         return hipGetLastError();
     }
     return run<128, 128, 2, 2, false, false, EPI>(p, s);
