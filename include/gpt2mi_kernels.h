@@ -131,16 +131,20 @@ int gpt2k_embedding_fwd(const int32_t* tok, const uint16_t* wte, const uint16_t*
 
 /*
  * Embedding backward: dwte[tok[r]] += dx[r]; dwpe[t] += sum_b dx[b*T + t]
- * (fp32 tables, bf16 dx).  Ids outside [0, V) are skipped.
+ * (fp32 tables, bf16 dx).  Ids outside [0, V) are skipped.  scratch: device
+ * bytes, at least gpt2k_scratch_bytes(5, B*T, V) (the rows are counting-sorted
+ * by token there); too small -> GPT2_E_SHAPE.  The additions into a table row
+ * come in no fixed order (runs that cross a sorting window add atomically).
  */
 int gpt2k_embedding_bwd(const int32_t* tok, const uint16_t* dx, float* dwte, float* dwpe, int32_t B, int32_t T,
-                        int32_t C, int32_t V, hipStream_t stream);
+                        int32_t C, int32_t V, void* scratch, int64_t scratch_bytes, hipStream_t stream);
 
 /*
  * Scratch bytes needed by the kernel-level calls, written to *out:
  * kind 1 = layernorm_bwd (a = rows, b = C); kind 2 = bias_gelu_bwd or
  * bias_grad (a = rows, b = N); kind 3 = gemm_tn_acc (a = M, b = N, c = K);
- * kind 4 = clip_adamw (a = n).  Unused arguments are ignored.
+ * kind 4 = clip_adamw (a = n); kind 5 = embedding_bwd (a = B*T, b = V).
+ * Unused arguments are ignored.
  */
 int gpt2k_scratch_bytes(int32_t kind, int64_t a, int64_t b, int64_t c, int64_t* out);
 

@@ -306,6 +306,40 @@ def test_embedding_parity(gpu_lib):
     assert np.all(host(dwte)[V:] == 0)
 
 
+def test_embedding_bwd_hot_tokens_and_invalid_ids(gpu_lib):
+    """Token-table scatter at the full batch (Zipf ids: token 0 covers ~14% of rows), plus
+    a batch where one id fills 300 rows (runs crossing many sorting windows) and ids
+    outside [0, V) that must be skipped."""
+    import torch
+    from transformer_lm_pretraining_amd import lib
+    C, V, Vp = 768, 50257, 50304
+    for case in ("zipf_full", "hot_invalid"):
+        if case == "zipf_full":
+            B, T = 19, 1024
+            tok, _ = synth.micro_batches(1, B, T, V, seed=11)[0]
+        else:
+            B, T = 2, 512
+            tok = np.ascontiguousarray(synth.micro_batches(1, B, T, V, seed=12)[0][0])
+            flat = tok.reshape(-1)
+            assert np.shares_memory(flat, tok)
+            flat[np.arange(5, 1024, 3)[:300]] = 7
+            flat[[0, 100, 777]] = [-1, V + 3, V]
+        say("embedding_bwd", case, B, T)
+        dx = bf16_round(synth.normal((B * T, C), seed=13))
+        dwte = to_dev_f32(np.zeros((Vp, C)))
+        dwpe = to_dev_f32(np.zeros((T, C)))
+        lib.embedding_bwd(to_dev_i32(tok), to_dev_bf16(dx), dwte, dwpe, V)
+        torch.cuda.synchronize()
+        valid = (tok.reshape(-1) >= 0) & (tok.reshape(-1) < V)
+        tok_ref = np.where(valid, tok.reshape(-1), 0).reshape(B, T)
+        dx_ref = np.where(valid[:, None], dx, 0.0).astype(np.float32)
+        rw, rp = ops.embedding_bwd(dx_ref.reshape(B, T, C), tok_ref, Vp, T)
+        _, rp = ops.embedding_bwd(dx.reshape(B, T, C), tok_ref, Vp, T)  # positions take every row
+        np.testing.assert_allclose(host(dwte), rw, rtol=1e-5, atol=1e-4)
+        np.testing.assert_allclose(host(dwpe), rp, rtol=1e-5, atol=1e-5)
+        assert np.all(host(dwte)[V:] == 0)
+
+
 # ---------------------------------------------------------------- clip + AdamW
 
 @pytest.mark.parametrize("gscale", [1e-4, 1.0])

@@ -95,8 +95,8 @@ struct ActsPlan {
 };
 struct ScratchPlan {
     int64_t flag, loss, scale, norm;  // header slots (256 B)
-    int64_t norm_partial, col_partial, splitk, dvec;
-    int64_t col_partial_elems, splitk_elems;
+    int64_t norm_partial, col_partial, splitk, dvec, emb_work;
+    int64_t col_partial_elems, splitk_elems, emb_work_elems;
     int64_t total;
 };
 
@@ -164,6 +164,9 @@ ScratchPlan plan_scratch(const gpt2_config& c) {
     off = align_up(off + s.splitk_elems * 4);
     s.dvec = off;
     off = align_up(off + (int64_t)c.B * c.H * c.T * 4);
+    s.emb_work_elems = embedding_bwd_work_elems(BT, c.V);
+    s.emb_work = off;
+    off = align_up(off + s.emb_work_elems * 4);
     s.total = off;
     return s;
 }
@@ -357,7 +360,8 @@ int run_backward(gpt2_handle* h, hipStream_t s) {
                                     h->act<float>(la.rstd1), d_res, 1, h->G(h->i_vec(l, 0)), h->G(h->i_vec(l, 1)),
                                     colp, BT, C, s));
     }
-    HIPCHK(launch_embedding_bwd(h->last_tok, d_res, h->G(h->i_wte()), h->G(h->i_wpe()), c.B, c.T, C, c.V, s));
+    HIPCHK(launch_embedding_bwd(h->last_tok, d_res, h->G(h->i_wte()), h->G(h->i_wpe()), c.B, c.T, C, c.V,
+                                (int32_t*)(h->S() + h->scr.emb_work), h->scr.emb_work_elems, s));
     return GPT2_OK;
 }
 
@@ -623,6 +627,7 @@ int gpt2k_scratch_bytes(int32_t kind, int64_t a, int64_t b, int64_t c, int64_t* 
         case 2: *out = colsum_partial_elems(a, (int)b) * 4; return GPT2_OK;
         case 3: *out = gemm_tn_partial_elems((int)a, (int)b, (int)c) * 4; return GPT2_OK;
         case 4: *out = adamw_partial_elems(a) * 8 + 256; return GPT2_OK;
+        case 5: *out = embedding_bwd_work_elems(a, (int)b) * 4; return GPT2_OK;
     }
     return GPT2_E_INVALID;
 }
@@ -750,9 +755,12 @@ int gpt2k_embedding_fwd(const int32_t* tok, const uint16_t* wte, const uint16_t*
 }
 
 int gpt2k_embedding_bwd(const int32_t* tok, const uint16_t* dx, float* dwte, float* dwpe, int32_t B, int32_t T,
-                        int32_t C, int32_t V, hipStream_t s) {
-    if (!tok || !dx || !dwte || !dwpe || B < 1 || T < 1 || C < 8 || C % 8 || V < 1) return GPT2_E_INVALID;
-    KCHK(launch_embedding_bwd(tok, dx, dwte, dwpe, B, T, C, V, s));
+                        int32_t C, int32_t V, void* scratch, int64_t scratch_bytes, hipStream_t s) {
+    if (!tok || !dx || !dwte || !dwpe || !scratch || B < 1 || T < 1 || C < 8 || C % 8 || V < 1 ||
+        (int64_t)B * T > INT32_MAX)
+        return GPT2_E_INVALID;
+    if (scratch_bytes < embedding_bwd_work_elems((int64_t)B * T, V) * 4) return GPT2_E_SHAPE;
+    KCHK(launch_embedding_bwd(tok, dx, dwte, dwpe, B, T, C, V, (int32_t*)scratch, scratch_bytes / 4, s));
     return GPT2_OK;
 }
 

@@ -111,31 +111,42 @@ __global__ void fold_colsum_kernel(const float* __restrict__ partial, int nblock
 
 constexpr int XE_THREADS = 512;
 
+// One row per workgroup, held in registers (NV 16-byte vectors per thread).
+// Three register passes: max, sum of exp, gradient.  Only the vector that
+// straddles V takes per-column bounds tests; whole vectors past V are padding
+// (gradient 0).  exp(x - m) is evaluated as 2^(x log2e - m log2e) (one FMA and
+// the hardware exp2).  The gradient pass writes p_j * dloss for every real
+// column; the owner of the target column then subtracts dloss there.
 template <int NV>
 __global__ __launch_bounds__(XE_THREADS) void xent_kernel(uint16_t* __restrict__ logits,
                                                           const int32_t* __restrict__ tgt,
                                                           float* __restrict__ loss_rows, int V, int Vp, float dloss,
                                                           int write_grad, int32_t* __restrict__ flag) {
     __shared__ float red[XE_THREADS / 64];
+    constexpr float L2E = 1.4426950408889634f;
     const int64_t row = blockIdx.x;
     u32x4* z = (u32x4*)(logits + row * (int64_t)Vp);
-    const int nvec = Vp / 8;
+    const int nvec = Vp / 8, nfull = V / 8;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     u32x4 v[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        int vid = tid + XE_THREADS * i;
+        const int vid = tid + XE_THREADS * i;
         v[i] = vid < nvec ? z[vid] : u32x4{0, 0, 0, 0};
     }
+    auto elem = [&](int i, int e) { return (e & 1) ? bfhi(v[i][e >> 1]) : bflo(v[i][e >> 1]); };
     // pass 1: row max over the real columns
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        int j0 = (tid + XE_THREADS * i) * 8;
+        const int vid = tid + XE_THREADS * i;
+        if (vid < nfull) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = (e & 1) ? bfhi(v[i][e >> 1]) : bflo(v[i][e >> 1]);
-            if (j0 + e < V) mx = fmaxf(mx, x);
+            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, elem(i, e));
+        } else if (vid * 8 < V) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (vid * 8 + e < V) mx = fmaxf(mx, elem(i, e));
         }
     }
     mx = wave_max(mx);
@@ -145,15 +156,19 @@ __global__ __launch_bounds__(XE_THREADS) void xent_kernel(uint16_t* __restrict__
 #pragma unroll
     for (int w = 1; w < XE_THREADS / 64; ++w) mx = fmaxf(mx, red[w]);
     __syncthreads();
+    const float mb = mx * L2E;
     // pass 2: sum of exp over the real columns
     float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        int j0 = (tid + XE_THREADS * i) * 8;
+        const int vid = tid + XE_THREADS * i;
+        if (vid < nfull) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = (e & 1) ? bfhi(v[i][e >> 1]) : bflo(v[i][e >> 1]);
-            if (j0 + e < V) sum += __expf(x - mx);
+            for (int e = 0; e < 8; ++e) sum += __builtin_amdgcn_exp2f(fmaf(elem(i, e), L2E, -mb));
+        } else if (vid * 8 < V) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (vid * 8 + e < V) sum += __builtin_amdgcn_exp2f(fmaf(elem(i, e), L2E, -mb));
         }
     }
     sum = wave_sum(sum);
@@ -170,26 +185,27 @@ __global__ __launch_bounds__(XE_THREADS) void xent_kernel(uint16_t* __restrict__
     if (tid == 0) loss_rows[row] = mx + logf(sum) - bf2f(logits[row * (int64_t)Vp + t]);
     if (!write_grad) return;
     __syncthreads();  // the target logit is read before any thread overwrites the row
-    const float inv = 1.0f / sum;
+    const float sc = dloss / sum;
+    const int tvid = t >> 3;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        int vid = tid + XE_THREADS * i;
+        const int vid = tid + XE_THREADS * i;
         if (vid >= nvec) break;
-        int j0 = vid * 8;
-        u32x4 o;
+        float d[8];
+        if (vid < nfull) {
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            float d[2];
+            for (int e = 0; e < 8; ++e) d[e] = __builtin_amdgcn_exp2f(fmaf(elem(i, e), L2E, -mb)) * sc;
+        } else {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                int j = j0 + 2 * e2 + h;
-                float x = h ? bfhi(v[i][e2]) : bflo(v[i][e2]);
-                float p = __expf(x - mx) * inv;
-                d[h] = j < V ? (p - (j == t ? 1.0f : 0.0f)) * dloss : 0.0f;
-            }
-            o[e2] = pack_bf2(d[0], d[1]);
+            for (int e = 0; e < 8; ++e)
+                d[e] = vid * 8 + e < V ? __builtin_amdgcn_exp2f(fmaf(elem(i, e), L2E, -mb)) * sc : 0.0f;
         }
-        z[vid] = o;
+        if (vid == tvid) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (e == (t & 7)) d[e] -= dloss;
+        }
+        z[vid] = u32x4{pack_bf2(d[0], d[1]), pack_bf2(d[2], d[3]), pack_bf2(d[4], d[5]), pack_bf2(d[6], d[7])};
     }
 }
 
@@ -234,24 +250,172 @@ __global__ __launch_bounds__(256) void embedding_fwd_kernel(const int32_t* __res
     }
 }
 
-__global__ __launch_bounds__(256) void embedding_bwd_wte_kernel(const int32_t* __restrict__ tok,
-                                                                const uint16_t* __restrict__ dx,
-                                                                float* __restrict__ dwte, int64_t rows, int C,
-                                                                int V) {
-    const int nv = C / 8;
-    const int64_t total = rows * nv;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = i / nv;
-        const int cv = (int)(i % nv);
-        const int id = tok[r];
-        if (id < 0 || id >= V) continue;
-        u32x4 g = *(const u32x4*)(dx + r * C + cv * 8);
-        float* d = dwte + (int64_t)id * C + cv * 8;
+// Token-table gradient: the rows are counting-sorted by token id (count,
+// scan, scatter), then each wave sums a window of EMB_WIN sorted rows run by
+// run.  A token occurring N times (Zipf: the most frequent id covers ~14% of a
+// batch) then costs about N / EMB_WIN additions to its table row instead of N
+// contending atomics.  The lanes of a wave that hold the same id are combined
+// before counting / claiming positions, so no counter sees more than one
+// atomic per wave.  A run that lies inside one window is the only writer of
+// its table row and read-modify-writes it; a run that crosses a window edge
+// adds atomically.  Ids outside [0, V) are left out.
+constexpr int EMB_WIN = 32;
+
+__global__ __launch_bounds__(256) void emb_zero_kernel(int32_t* __restrict__ p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void emb_count_kernel(const int32_t* __restrict__ tok, int64_t rows, int V,
+                                                        int32_t* __restrict__ counts) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int t = i < rows ? tok[i] : -1;
+    bool active = t >= 0 && t < V;
+    while (true) {
+        const uint64_t act = __ballot(active);
+        if (act == 0) break;
+        const int leader = __ffsll((unsigned long long)act) - 1;
+        const int lt = __shfl(t, leader, WAVE);
+        const uint64_t same = __ballot(active && t == lt);
+        if (lane == leader) atomicAdd(counts + lt, (int)__popcll(same));
+        if (active && t == lt) active = false;
+    }
+}
+
+// Exclusive prefix sum of counts[0..V) into start[0..V] (start[V] = total) and
+// cursor[0..V); one workgroup, V <= 65536.  Thread tid owns the 4 counts at
+// 4096*i + 4*tid; a group of 8 such slices is loaded up front, then each
+// 4096-count slice is scanned with wavefront shuffles and a 16-entry scan of
+// the wave totals.
+__global__ __launch_bounds__(1024) void emb_scan_kernel(const int32_t* __restrict__ counts, int V,
+                                                        int32_t* __restrict__ start, int32_t* __restrict__ cursor) {
+    constexpr int GROUP = 8;
+    __shared__ int wsum[2][16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int carry = 0;
+    for (int g0 = 0; g0 < V; g0 += GROUP * 4096) {
+        int c[GROUP][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            unsafeAtomicAdd(d + 2 * e, bflo(g[e]));
-            unsafeAtomicAdd(d + 2 * e + 1, bfhi(g[e]));
+        for (int i = 0; i < GROUP; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int k = g0 + i * 4096 + tid * 4 + e;
+                c[i][e] = k < V ? counts[k] : 0;
+            }
+#pragma unroll
+        for (int i = 0; i < GROUP; ++i) {
+            const int s0 = g0 + i * 4096;
+            if (s0 >= V) break;
+            const int tsum = c[i][0] + c[i][1] + c[i][2] + c[i][3];
+            int x = tsum;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(x, o, WAVE);
+                if (lane >= o) x += y;
+            }
+            if (lane == 63) wsum[i & 1][wave] = x;
+            __syncthreads();
+            int w = lane < 16 ? wsum[i & 1][lane] : 0;
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) {
+                const int y = __shfl_up(w, o, WAVE);
+                if (lane >= o) w += y;
+            }
+            const int before = __shfl(w, wave > 0 ? wave - 1 : 0, WAVE);
+            const int total = __shfl(w, 15, WAVE);
+            int run = carry + (wave > 0 ? before : 0) + x - tsum;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int k = s0 + tid * 4 + e;
+                if (k < V) {
+                    start[k] = run;
+                    cursor[k] = run;
+                }
+                run += c[i][e];
+            }
+            carry += total;
         }
+    }
+    if (tid == 0) start[V] = carry;
+}
+
+__global__ __launch_bounds__(256) void emb_scatter_kernel(const int32_t* __restrict__ tok, int64_t rows, int V,
+                                                          int32_t* __restrict__ cursor, int32_t* __restrict__ order,
+                                                          int32_t* __restrict__ stok) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int t = i < rows ? tok[i] : -1;
+    bool active = t >= 0 && t < V;
+    while (true) {
+        const uint64_t act = __ballot(active);
+        if (act == 0) break;
+        const int leader = __ffsll((unsigned long long)act) - 1;
+        const int lt = __shfl(t, leader, WAVE);
+        const uint64_t same = __ballot(active && t == lt);
+        int base = 0;
+        if (lane == leader) base = atomicAdd(cursor + lt, (int)__popcll(same));
+        base = __shfl(base, leader, WAVE);
+        if (active && t == lt) {
+            const int pos = base + (int)__popcll(same & ((1ull << lane) - 1ull));
+            order[pos] = (int)i;
+            stok[pos] = lt;
+            active = false;
+        }
+    }
+}
+
+// One wave per window of EMB_WIN sorted rows; each lane owns 4 columns per pass.
+__global__ __launch_bounds__(256) void emb_segsum_kernel(const int32_t* __restrict__ order,
+                                                         const int32_t* __restrict__ stok,
+                                                         const int32_t* __restrict__ start, int V,
+                                                         const uint16_t* __restrict__ dx, int C,
+                                                         float* __restrict__ dwte) {
+    const int n = start[V];
+    const int wv = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * 256 + threadIdx.x) >> 6));
+    const int lane = threadIdx.x & 63;
+    const int p0 = wv * EMB_WIN;
+    if (p0 >= n) return;
+    const int p1 = min(p0 + EMB_WIN, n);
+    const bool head_shared = p0 > 0 && stok[p0 - 1] == stok[p0];
+    const bool tail_shared = p1 < n && stok[p1] == stok[p1 - 1];
+    for (int c4 = lane; c4 < C / 4; c4 += 64) {
+        u32x2 gv[EMB_WIN];
+#pragma unroll
+        for (int q = 0; q < EMB_WIN; ++q)
+            if (p0 + q < p1) gv[q] = *(const u32x2*)(dx + (int64_t)order[p0 + q] * C + c4 * 4);
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        int cur = stok[p0];
+        bool shared = head_shared;
+        auto flush = [&](bool sh) {
+            float* d = dwte + (int64_t)cur * C + c4 * 4;
+            if (sh) {
+                unsafeAtomicAdd(d, acc.x);
+                unsafeAtomicAdd(d + 1, acc.y);
+                unsafeAtomicAdd(d + 2, acc.z);
+                unsafeAtomicAdd(d + 3, acc.w);
+            } else {
+                float4 o = *(float4*)d;
+                o.x += acc.x; o.y += acc.y; o.z += acc.z; o.w += acc.w;
+                *(float4*)d = o;
+            }
+        };
+#pragma unroll
+        for (int q = 0; q < EMB_WIN; ++q) {
+            if (p0 + q >= p1) break;
+            const int t = stok[p0 + q];
+            if (t != cur) {
+                flush(shared);
+                acc = make_float4(0.f, 0.f, 0.f, 0.f);
+                cur = t;
+                shared = false;
+            }
+            acc.x += bflo(gv[q].x);
+            acc.y += bfhi(gv[q].x);
+            acc.z += bflo(gv[q].y);
+            acc.w += bfhi(gv[q].y);
+        }
+        flush(shared || tail_shared);
     }
 }
 
@@ -336,11 +500,28 @@ hipError_t launch_embedding_fwd(const int32_t* tok, const uint16_t* wte, const u
     return hipGetLastError();
 }
 
+int64_t embedding_bwd_work_elems(int64_t rows, int V) { return 3 * (int64_t)V + 1 + 2 * rows; }
+
 hipError_t launch_embedding_bwd(const int32_t* tok, const uint16_t* dx, float* dwte, float* dwpe, int B, int T,
-                                int C, int V, hipStream_t s) {
-    int64_t rows = (int64_t)B * T;
-    PROF_LAUNCH(KC_EMB_BWD_WTE, 10.0 * rows * C, s, hipLaunchKernelGGL(embedding_bwd_wte_kernel, dim3(grid_for(rows * (C / 8))), dim3(256), 0, s, tok, dx, dwte, rows,
-                       C, V));
+                                int C, int V, int32_t* work, int64_t work_elems, hipStream_t s) {
+    const int64_t rows = (int64_t)B * T;
+    if (C % 4 || V > 65536 || work == nullptr || work_elems < embedding_bwd_work_elems(rows, V) || rows > INT32_MAX)
+        return hipErrorInvalidValue;
+    int32_t* counts = work;
+    int32_t* start = counts + V;
+    int32_t* cursor = start + V + 1;
+    int32_t* order = cursor + V;
+    int32_t* stok = order + rows;
+    const int rb = (int)cdiv(rows, 256);
+    const int nwin = (int)cdiv(rows, EMB_WIN);
+    PROF_LAUNCH(KC_EMB_BWD_WTE, 4.0 * rows * C + 8.0 * rows * C, s, {
+        hipLaunchKernelGGL(emb_zero_kernel, dim3(cdiv(V, 256)), dim3(256), 0, s, counts, V);
+        hipLaunchKernelGGL(emb_count_kernel, dim3(rb), dim3(256), 0, s, tok, rows, V, counts);
+        hipLaunchKernelGGL(emb_scan_kernel, dim3(1), dim3(1024), 0, s, counts, V, start, cursor);
+        hipLaunchKernelGGL(emb_scatter_kernel, dim3(rb), dim3(256), 0, s, tok, rows, V, cursor, order, stok);
+        hipLaunchKernelGGL(emb_segsum_kernel, dim3(cdiv(nwin, 4)), dim3(256), 0, s, order, stok, start, V, dx, C,
+                           dwte);
+    });
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     PROF_LAUNCH(KC_EMB_BWD_WPE, 2.0 * rows * C + 8.0 * T * C, s, hipLaunchKernelGGL(embedding_bwd_wpe_kernel, dim3(grid_for((int64_t)T * C)), dim3(256), 0, s, dx, dwpe, B, T, C));

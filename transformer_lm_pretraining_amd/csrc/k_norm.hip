@@ -77,6 +77,9 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const uint16_t* __restrict_
     }
 }
 
+// Each wave walks rows with a grid stride and keeps the next row's loads (x,
+// dy and, when accumulating, the residual gradient) in flight while it
+// computes the current one.
 template <int VEC, int NV>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy,
                                                      const float* __restrict__ w, const float* __restrict__ mean,
@@ -96,20 +99,33 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const uint16_t* __restrict_
             dw_acc[j][e] = 0.f;
             db_acc[j][e] = 0.f;
         }
-    const int64_t stride = (int64_t)gridDim.x * ROWS_PER_BLOCK;
-    for (int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + wave; row < rows; row += stride) {
+    struct RowIn {
+        VT xv[NV], gv[NV], rv[NV];
+        float mu, rs;
+    };
+    auto load = [&](int64_t row, RowIn& in) {
         const VT* xr = (const VT*)(x + row * C);
         const VT* dyr = (const VT*)(dy + row * C);
-        const float mu = mean[row], rs = rstd[row];
+        const VT* dr = (const VT*)(dres + row * C);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            in.xv[j] = xr[j * 64 + lane];
+            in.gv[j] = dyr[j * 64 + lane];
+            if (accumulate) in.rv[j] = dr[j * 64 + lane];
+        }
+        in.mu = mean[row];
+        in.rs = rstd[row];
+    };
+    auto compute = [&](int64_t row, const RowIn& in) {
         float xh[NV][VEC], g[NV][VEC], wdy[NV][VEC];
         float s1 = 0.f, s2 = 0.f;
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-            Vec<VEC>::unpack(xr[j * 64 + lane], xh[j]);
-            Vec<VEC>::unpack(dyr[j * 64 + lane], g[j]);
+            Vec<VEC>::unpack(in.xv[j], xh[j]);
+            Vec<VEC>::unpack(in.gv[j], g[j]);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                xh[j][e] = (xh[j][e] - mu) * rs;
+                xh[j][e] = (xh[j][e] - in.mu) * in.rs;
                 wdy[j][e] = wv[j][e] * g[j][e];
                 s1 += wdy[j][e];
                 s2 += wdy[j][e] * xh[j][e];
@@ -123,14 +139,28 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const uint16_t* __restrict_
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             float o[VEC], prev[VEC];
-            if (accumulate) Vec<VEC>::unpack(dr[j * 64 + lane], prev);
+            if (accumulate) Vec<VEC>::unpack(in.rv[j], prev);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                o[e] = (wdy[j][e] - s1 - xh[j][e] * s2) * rs;
+                o[e] = (wdy[j][e] - s1 - xh[j][e] * s2) * in.rs;
                 if (accumulate) o[e] += prev[e];
             }
             dr[j * 64 + lane] = Vec<VEC>::pack(o);
         }
+    };
+    const int64_t stride = (int64_t)gridDim.x * ROWS_PER_BLOCK;
+    int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + wave;
+    RowIn a, b;
+    if (row < rows) load(row, a);
+    while (row < rows) {
+        const int64_t r1 = row + stride;
+        if (r1 < rows) load(r1, b);
+        compute(row, a);
+        if (r1 >= rows) break;
+        const int64_t r2 = r1 + stride;
+        if (r2 < rows) load(r2, a);
+        compute(r1, b);
+        row = r2;
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j)
@@ -172,7 +202,7 @@ __global__ __launch_bounds__(256) void fold_partials_kernel(const float* __restr
         unsafeAtomicAdd(out1 + c - C, t);
 }
 
-int ln_blocks(int64_t rows) { return (int)std::min<int64_t>(512, cdiv(rows, ROWS_PER_BLOCK)); }
+int ln_blocks(int64_t rows) { return (int)std::min<int64_t>(768, cdiv(rows, ROWS_PER_BLOCK)); }
 
 template <int VEC, int NV>
 hipError_t ln_fwd_t(const uint16_t* x, const float* w, const float* b, uint16_t* y, float* mean, float* rstd,

@@ -43,8 +43,10 @@ hipError_t launch_xent(uint16_t* logits, const int32_t* tgt, float* loss_rows, i
 hipError_t launch_mean(const float* x, int64_t n, float* out, hipStream_t s);
 hipError_t launch_embedding_fwd(const int32_t* tok, const uint16_t* wte, const uint16_t* wpe, uint16_t* x, int B,
                                 int T, int C, int V, int32_t* flag, hipStream_t s);
+// work: embedding_bwd_work_elems(B*T, V) int32 scratch (counting sort of the rows by token)
+int64_t embedding_bwd_work_elems(int64_t rows, int V);
 hipError_t launch_embedding_bwd(const int32_t* tok, const uint16_t* dx, float* dwte, float* dwpe, int B, int T,
-                                int C, int V, hipStream_t s);
+                                int C, int V, int32_t* work, int64_t work_elems, hipStream_t s);
 
 // ---- attention (k_attn.hip) --------------------------------------------------
 hipError_t launch_attention_fwd(const uint16_t* qkv, uint16_t* out, float* lse, int B, int T, int H, int C,

@@ -89,7 +89,7 @@ _SIGS = {
     "gpt2k_clip_adamw": (c_int32, [c_void_p] * 5 + [c_int64, c_int64, POINTER(AdamwArgs), c_void_p, c_void_p,
                                                     c_int64, c_void_p]),
     "gpt2k_embedding_fwd": (c_int32, [c_void_p] * 4 + [c_int32] * 4 + [c_void_p, c_void_p]),
-    "gpt2k_embedding_bwd": (c_int32, [c_void_p] * 4 + [c_int32] * 4 + [c_void_p]),
+    "gpt2k_embedding_bwd": (c_int32, [c_void_p] * 4 + [c_int32] * 4 + [c_void_p, c_int64, c_void_p]),
     "gpt2k_scratch_bytes": (c_int32, [c_int32, c_int64, c_int64, c_int64, POINTER(c_int64)]),
 }
 
@@ -416,5 +416,6 @@ def embedding_fwd(tok, wte, wpe, V, flag=None):
 def embedding_bwd(tok, dx, dwte, dwpe, V):
     B, T = tok.shape
     C = dx.shape[1]
-    check(load().gpt2k_embedding_bwd(_ptr(tok), _ptr(dx), _ptr(dwte), _ptr(dwpe), B, T, C, V, _stream()),
-          "gpt2k_embedding_bwd")
+    s = _scratch(scratch_bytes(5, B * T, V), dx.device)
+    check(load().gpt2k_embedding_bwd(_ptr(tok), _ptr(dx), _ptr(dwte), _ptr(dwpe), B, T, C, V, _ptr(s), s.numel(),
+                                     _stream()), "gpt2k_embedding_bwd")
