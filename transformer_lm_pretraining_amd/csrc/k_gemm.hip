@@ -10,7 +10,7 @@
 //     are read transposed out of LDS (ds_read_b64_tr_b16).  The bias gradient
 //     (column sums of dY) is folded into the same pass: the workgroups of the
 //     first output column tile sum the dY fragments they read anyway.
-// Large problems run 256x256 tiles (gemm_nt_pipe_kernel, gemm_tn_pipe_kernel):
+// Large problems run 256x256 tiles (gemm_nt_w8_kernel, gemm_tn_pipe_kernel):
 // operands go global -> LDS without register staging, several stages in
 // flight.  Small ones run the generic BM x BN kernel (gemm_kernel: register
 // prefetch, LDS double buffer, rows padded to 72 bf16).  Workgroups are
@@ -283,21 +283,16 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* src, uint16_t* dst_wav
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined NT tiles: 256x256 per workgroup, four 128x128 wave tiles, the
-// reduction walked in stages of 32.  NS stage buffers live in LDS and NS-1 of
-// them are in flight while one is consumed, so each CU keeps 96-128 KB of
-// loads outstanding (the loaded memory latency is about 1-2 us, the MFMA time
-// of a stage about 0.4 us).  Each wave instruction of
-// global_load_lds_dwordx4 fills 1 KB = 16 rows of 32 bf16; the 16-byte
-// vector c of row r sits at slot c ^ ((r >> 2) & 3) so the fragment reads of
-// 16 consecutive rows hit 16 distinct 16-byte bank groups.  Waits count
-// outstanding loads (vmcnt) per stage, and the one barrier per stage sits
-// between the two halves of the last MFMA group, with the next stage's first
-// fragments read right after it.  The bias is loaded into the accumulators
-// before the first MFMA.  The MFMA takes B as its first operand, so a lane's
-// accumulator holds 4 consecutive output columns of one output row.
+// Shared pieces of the pipelined 256x256 kernels.  Stage depth and count are
+// build-time constants (NT: 2 stages of 64 reduction columns; TN: 4 of 32 tokens).
 #ifndef NT_STAGES
-#define NT_STAGES 4
+#define NT_STAGES 2
+#endif
+#ifndef NT_KD
+#define NT_KD 64
+#endif
+#ifndef TN_STAGES
+#define TN_STAGES 4
 #endif
 constexpr int PBK = 32;                  // reduction depth of one stage
 constexpr int PSTAGE = 2 * BIG * PBK;    // A and B tiles of one stage, bf16 elements (32 KB)
@@ -311,24 +306,50 @@ __device__ __forceinline__ float acc_read(float x) {
     return r;
 }
 
-// Wait until at most n stage groups (8 loads per wave each) are still in flight.
+// s_waitcnt immediate waiting for vmcnt <= n (expcnt and lgkmcnt left alone):
+// vmcnt[3:0] | expcnt[6:4] = 7 | lgkmcnt[11:8] = 15 | vmcnt[5:4] at [15:14].
+constexpr int vm_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+// Wait until at most n stage groups of G loads per wave are still in flight.
+template <int G>
 __device__ __forceinline__ void wait_stage_groups(int n) {
-    // s_waitcnt immediate: vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt[5:4] at [15:14]
     switch (n) {
-        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-        case 1: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-        case 2: __builtin_amdgcn_s_waitcnt(0x4F70); break;
-        case 3: __builtin_amdgcn_s_waitcnt(0x4F78); break;
-        default: __builtin_amdgcn_s_waitcnt(0x8F70); break;
+        case 0: __builtin_amdgcn_s_waitcnt(vm_imm(0)); break;
+        case 1: __builtin_amdgcn_s_waitcnt(vm_imm(G)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(vm_imm(2 * G)); break;
+        case 3: __builtin_amdgcn_s_waitcnt(vm_imm(3 * G)); break;
+        default: __builtin_amdgcn_s_waitcnt(vm_imm(4 * G)); break;
     }
 }
 
-template <int EPI, int NS>
-__global__ __launch_bounds__(256, 1) void gemm_nt_pipe_kernel(GemmParams p) {
-    static_assert(NS >= 4 && NS <= 5, "the epilogue reuses 128 KB of stage buffers");
-    __shared__ __attribute__((aligned(16))) uint16_t smem[NS * PSTAGE];
+// ---------------------------------------------------------------------------
+// NT tiles with eight waves: 256x256 per workgroup of 512 threads, wave grid
+// 2 (rows) x 4 (columns) of 128x64 wave tiles (128 accumulators per lane, two
+// waves per SIMD).  Each wave sustains only ~10-12 GB/s of loads into LDS, so
+// eight issuing waves are needed to feed 256x256 tiles; the second wave on each
+// SIMD also hides the other's barrier and LDS waits.  A stage holds KD
+// reduction columns (rows of 2*KD bytes; 128-byte rows make every L2 request
+// a full line), NS stages in LDS.  The 16-byte vector c of a row r sits at
+// slot c ^ swz(r) so the fragment reads of 16 consecutive rows hit distinct
+// bank groups.  Waits, barrier placement and epilogue as in the 4-wave kernel.
+template <int KD>
+struct NtStage {
+    static constexpr int CPR = KD / 8;                // 16-byte vectors per row
+    static constexpr int RPI = 64 / CPR;              // rows per 1 KB load instruction
+    static constexpr int ELEMS = 2 * BIG * KD;        // A and B tiles, bf16 elements
+    static constexpr int KS = KD / 16;                // MFMA k-steps per stage
+    __device__ static int swz(int r) { return CPR == 4 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
+};
+
+template <int EPI, int NS, int KD>
+__global__ __launch_bounds__(512, 1) void gemm_nt_w8_kernel(GemmParams p) {
+    typedef NtStage<KD> St;
+    static_assert(NS * St::ELEMS >= BIG * BIG, "the epilogue reuses 128 KB of stage buffers");
+    static_assert(NS * St::ELEMS * 2 <= 160 * 1024, "LDS");
+    constexpr int IPO = BIG / St::RPI / 8;            // load instructions per wave per operand
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NS * St::ELEMS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
 
     const int ntiles = p.tiles_m * p.tiles_n;
     int pid = blockIdx.x;
@@ -338,47 +359,48 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_pipe_kernel(GemmParams p) {
     const int gsize = min(p.tiles_m - first_m, GROUP_M);
     const int m0 = (first_m + (pid % in_group) % gsize) * BIG;
     const int n0 = ((pid % in_group) / gsize) * BIG;
-    const int nk = p.nk_total * (BK / PBK);
+    const int nk = p.nk_total * (BK / KD);
 
-    // Lane q of load instruction i covers row 64*wave + 16*i + q/4 at physical
-    // slot q&3, i.e. logical vector (q&3) ^ ((q>>4)&3).  Rows past M / N are
-    // clamped (their products are never stored).  Offsets are 32-bit elements
-    // (the host checks M*lda and N*ldb < 2^31).
-    const int lvec = ((lane & 3) ^ ((lane >> 4) & 3)) << 3;
-    uint32_t offA[4], offB[4];
+    // Lane q of load instruction i covers row (wave*IPO + i)*RPI + q/CPR at
+    // physical slot q%CPR, i.e. logical vector (q%CPR) ^ swz(row).  Rows past
+    // M / N are clamped (their products are never stored).  Offsets are 32-bit
+    // elements (the host checks M*lda and N*ldb < 2^31).
+    uint32_t offA[IPO], offB[IPO];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        offA[i] = (uint32_t)min(m0 + wave * 64 + 16 * i + (lane >> 2), p.M - 1) * (uint32_t)p.lda + lvec;
-        offB[i] = (uint32_t)min(n0 + wave * 64 + 16 * i + (lane >> 2), p.N - 1) * (uint32_t)p.ldb + lvec;
+    for (int i = 0; i < IPO; ++i) {
+        const int row = (wave * IPO + i) * St::RPI + lane / St::CPR;
+        const int lv = ((lane % St::CPR) ^ St::swz(row)) << 3;
+        offA[i] = (uint32_t)min(m0 + row, p.M - 1) * (uint32_t)p.lda + lv;
+        offB[i] = (uint32_t)min(n0 + row, p.N - 1) * (uint32_t)p.ldb + lv;
     }
     auto issue = [&](int t) {
-        uint16_t* sa = smem + (t % NS) * PSTAGE;
-        uint16_t* sb = sa + BIG * PBK;
-        const uint32_t k0 = (uint32_t)t * PBK;
+        uint16_t* sa = smem + (t % NS) * St::ELEMS;
+        uint16_t* sb = sa + BIG * KD;
+        const uint32_t k0 = (uint32_t)t * KD;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_dma16(p.A + (offA[i] + k0), sa + (wave * 64 + 16 * i) * PBK);
+        for (int i = 0; i < IPO; ++i) lds_dma16(p.A + (offA[i] + k0), sa + (wave * IPO + i) * 512);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_dma16(p.B + (offB[i] + k0), sb + (wave * 64 + 16 * i) * PBK);
+        for (int i = 0; i < IPO; ++i) lds_dma16(p.B + (offB[i] + k0), sb + (wave * IPO + i) * 512);
     };
 
-    // prologue: the first NS-1 stages in flight (nk >= 1: the host requires K >= 64)
+    // prologue: all NS stage buffers in flight (nk >= 1: the host requires K >= 64)
 #pragma unroll
-    for (int t = 0; t < NS - 1; ++t)
+    for (int t = 0; t < NS; ++t)
         if (t < nk) issue(t);
     __builtin_amdgcn_sched_barrier(0);
-    // bias of this lane's 16 column groups (zero past N; N % 8 == 0 keeps a group whole)
-    float4 b4[4][4];
+    // bias of this lane's 8 column groups (zero past N; N % 8 == 0 keeps a group whole)
+    float4 b4[2][4];
     if ((EPI == EPI_BF16 || EPI == EPI_BF16R || EPI == EPI_GELU) && p.bias != nullptr) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg)
-                b4[j][rg] = *(const float4*)(p.bias + min(n0 + wn * 128 + j * 32 + 8 * rg + 4 * g, p.N - 4));
+                b4[j][rg] = *(const float4*)(p.bias + min(n0 + wn * 64 + j * 32 + 8 * rg + 4 * g, p.N - 4));
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-                const bool in = n0 + wn * 128 + j * 32 + 8 * rg + 4 * g < p.N;
+                const bool in = n0 + wn * 64 + j * 32 + 8 * rg + 4 * g < p.N;
                 b4[j][rg].x = in ? b4[j][rg].x : 0.f;
                 b4[j][rg].y = in ? b4[j][rg].y : 0.f;
                 b4[j][rg].z = in ? b4[j][rg].z : 0.f;
@@ -386,18 +408,17 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_pipe_kernel(GemmParams p) {
             }
     } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) b4[j][rg] = float4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // accumulators start at the bias of their columns.
-    // acc[i][j][4*rg + e] is C[m0 + wm*128 + i*32 + (lane&31)][n0 + wn*128 + j*32 + 8*rg + 4*g + e].
-    floatx16 acc[4][4];
+    // acc[i][j][4*rg + e] is C[m0 + wm*128 + i*32 + (lane&31)][n0 + wn*64 + j*32 + 8*rg + 4*g + e].
+    floatx16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 acc[i][j][4 * rg + 0] = b4[j][rg].x;
@@ -405,94 +426,79 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_pipe_kernel(GemmParams p) {
                 acc[i][j][4 * rg + 2] = b4[j][rg].z;
                 acc[i][j][4 * rg + 3] = b4[j][rg].w;
             }
-    wait_stage_groups(min(NS - 1, nk) - 1);
+    wait_stage_groups<2 * IPO>(min(NS, nk) - 1);
     __syncthreads();
 
-    // Fragment rows are fixed per lane; the two 16-deep halves of a stage are
-    // vectors g and 2+g, swizzled by the row's (r>>2)&3 (rows are 32-aligned + lane&31).
+    // fragment rows are fixed per lane (32-aligned + lane&31); k-step kk reads vector 2*kk + g
     const int fr = lane & 31;
-    const int cv0 = (g ^ ((fr >> 2) & 3)) << 3, cv1 = cv0 ^ 16;
-    const int ra = (wm * 128 + fr) * PBK, rb = (wn * 128 + fr) * PBK;
-    bf16x8 af[2][4], bfr[2][4];
+    const int sw = St::swz(fr);
+    const int ra = (wm * 128 + fr) * KD, rb = BIG * KD + (wn * 64 + fr) * KD;
+    auto cvec = [&](int kk) { return ((2 * kk + g) ^ sw) << 3; };
+    bf16x8 af[2][4], bfr[2][2];
+    auto read = [&](const uint16_t* st, int kk, int b) {
+        const int cv = cvec(kk);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[0][i] = *(const bf16x8*)(smem + ra + i * 32 * PBK + cv0);
+        for (int i = 0; i < 4; ++i) af[b][i] = *(const bf16x8*)(st + ra + i * 32 * KD + cv);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bfr[0][j] = *(const bf16x8*)(smem + BIG * PBK + rb + j * 32 * PBK + cv0);
+        for (int j = 0; j < 2; ++j) bfr[b][j] = *(const bf16x8*)(st + rb + j * 32 * KD + cv);
+    };
+    auto mma = [&](int b, int i0) {
+#pragma unroll
+        for (int i = i0; i < i0 + 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(bfr[b][j], af[b][i], acc[i][j]);
+    };
+    read(smem, 0, 0);
     int s = 0;
     do {
-        const uint16_t* sa = smem + (s % NS) * PSTAGE;
-        const uint16_t* sb = sa + BIG * PBK;
-        // first half of the stage (fragments [0]); the second half's are read meanwhile
+        const uint16_t* st = smem + (s % NS) * St::ELEMS;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(bfr[0][j], af[0][i], acc[i][j]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[1][i] = *(const bf16x8*)(sa + ra + i * 32 * PBK + cv1);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bfr[1][j] = *(const bf16x8*)(sb + rb + j * 32 * PBK + cv1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 2; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(bfr[0][j], af[0][i], acc[i][j]);
-        __builtin_amdgcn_sched_barrier(0);
-        // second half (fragments [1])
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(bfr[1][j], af[1][i], acc[i][j]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (s + 1 < nk) {
-            // stage s+1 has landed once only the stages issued after it remain in flight
-            wait_stage_groups(min(s + NS - 2, nk - 1) - (s + 1));
-            __syncthreads();
-            // every wave is past stage s-1, whose buffer takes stage s+NS-1
-            if (s + NS - 1 < nk) issue(s + NS - 1);
-            const uint16_t* na = smem + ((s + 1) % NS) * PSTAGE;
-            const uint16_t* nb = na + BIG * PBK;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) af[0][i] = *(const bf16x8*)(na + ra + i * 32 * PBK + cv0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bfr[0][j] = *(const bf16x8*)(nb + rb + j * 32 * PBK + cv0);
+        for (int kk = 0; kk < St::KS; ++kk) {
+            const int b = kk & 1;
+            mma(b, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kk + 1 < St::KS) {
+                read(st, kk + 1, b ^ 1);
+            } else if (s + 1 < nk) {
+                // stage s+1 has landed once only the stages issued after it remain in flight
+                wait_stage_groups<2 * IPO>(min(s + NS - 1, nk - 1) - (s + 1));
+                __syncthreads();
+                // every wave has read all of stage s (its last fragments are in
+                // registers): its buffer takes stage s+NS
+                if (s + NS < nk) issue(s + NS);
+                read(smem + ((s + 1) % NS) * St::ELEMS, 0, b ^ 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            mma(b, 2);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 2; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(bfr[1][j], af[1][i], acc[i][j]);
-        __builtin_amdgcn_sched_barrier(0);
     } while (++s < nk);
-    // all fragment reads done: the stage buffers become the output tile (the
-    // barrier also covers the MFMA -> accumulator-read latency)
     __syncthreads();
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
-    // The epilogue's second input (residual, or GELU's pre-activation) is read
-    // for the whole tile now, so its latency overlaps the staging below.  Thread
-    // tid covers 16-byte chunk (tid & 31) of rows 8*it + tid/32, it = 0..31.
-    constexpr int EIT = BIG * BIG / 8 / 256;
+    // second epilogue input for the whole tile, read now so its latency overlaps
+    // the staging: thread tid covers 16-byte chunk (tid & 31) of rows 16*it + tid/32.
+    constexpr int EIT = BIG * BIG / 8 / 512;
     constexpr bool HAS_IN = EPI == EPI_DGELU || EPI == EPI_BF16R;
     u32x4 pin[HAS_IN ? EIT : 1];
     if constexpr (HAS_IN) {
 #pragma unroll
         for (int it = 0; it < EIT; ++it) {
-            const int grow = m0 + it * 8 + (tid >> 5), gcol = n0 + (tid & 31) * 8;
+            const int grow = m0 + it * 16 + (tid >> 5), gcol = n0 + (tid & 31) * 8;
             pin[it] = (grow < p.M && gcol < p.N) ? *(const u32x4*)(p.res + (int64_t)grow * p.ldr + gcol) : u32x4{0u, 0u, 0u, 0u};
         }
     }
 
-    // stage 1: acc -> bf16 tile [256][256] in LDS.
+    // stage 1: acc -> bf16 tile [256][256] in LDS (16-byte chunks XOR-swizzled by row)
     uint16_t* so = smem;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = wm * 128 + i * 32 + fr;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-                const int col = wn * 128 + j * 32 + 8 * rg + 4 * g;
+                const int col = wn * 64 + j * 32 + 8 * rg + 4 * g;
                 const int chunk = (col >> 3) ^ (row & 31);
                 *(u32x2*)(so + row * BIG + chunk * 8 + (col & 7)) =
                     u32x2{pack_bf2(acc_read(acc[i][j][4 * rg]), acc_read(acc[i][j][4 * rg + 1])),
@@ -502,7 +508,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_pipe_kernel(GemmParams p) {
     __syncthreads();
     // stage 2: coalesced 16-byte row segments
     auto out_chunk = [&](int it) {
-        const int row = it * 8 + (tid >> 5), chunk = tid & 31;
+        const int row = it * 16 + (tid >> 5), chunk = tid & 31;
         const int grow = m0 + row, gcol = n0 + chunk * 8;
         if (grow >= p.M || gcol >= p.N) return;
         u32x4 w = *(const u32x4*)(so + row * BIG + ((chunk ^ (row & 31)) << 3));
@@ -623,7 +629,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_pipe_kernel(GemmParams p) {
     };
 
 #pragma unroll
-    for (int t = 0; t < NS - 1; ++t)
+    for (int t = 0; t < NS; ++t)
         if (t < nk) issue(t);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -636,7 +642,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_pipe_kernel(GemmParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     float bsum[4] = {0.f, 0.f, 0.f, 0.f};
-    wait_stage_groups(min(NS - 1, nk) - 1);
+    wait_stage_groups<8>(min(NS, nk) - 1);
     __syncthreads();
 
     // per-lane fragment addresses within a stage tile (token row 4g + (lane&15)/4,
@@ -691,9 +697,10 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_pipe_kernel(GemmParams p) {
             for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(xf[1][j], dyf[1][i], acc[i][j]);
         __builtin_amdgcn_sched_barrier(0);
         if (s + 1 < nk) {
-            wait_stage_groups(min(s + NS - 2, nk - 1) - (s + 1));
+            wait_stage_groups<8>(min(s + NS - 1, nk - 1) - (s + 1));
             __syncthreads();
-            if (s + NS - 1 < nk) issue(s + NS - 1);
+            // all of stage s is in registers: its buffer takes stage s+NS
+            if (s + NS < nk) issue(s + NS);
             read_frags(smem + ((s + 1) % NS) * PSTAGE, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -796,12 +803,12 @@ hipError_t run_nt(GemmParams p, hipStream_t s) {
         const double work = 2.0 * p.M * p.N * (double)p.nk_total * BK;
         if (EPI == EPI_BF16 && p.res != nullptr)
             PROF_LAUNCH(gemm_class(false, EPI), work, s,
-                        hipLaunchKernelGGL((gemm_nt_pipe_kernel<EPI_BF16R, NT_STAGES>), dim3(p.tiles_m * p.tiles_n),
-                                           dim3(256), 0, s, p));
+                        hipLaunchKernelGGL((gemm_nt_w8_kernel<EPI_BF16R, NT_STAGES, NT_KD>), dim3(p.tiles_m * p.tiles_n),
+                                           dim3(512), 0, s, p));
         else
             PROF_LAUNCH(gemm_class(false, EPI), work, s,
-                        hipLaunchKernelGGL((gemm_nt_pipe_kernel<EPI, NT_STAGES>), dim3(p.tiles_m * p.tiles_n),
-                                           dim3(256), 0, s, p));
+                        hipLaunchKernelGGL((gemm_nt_w8_kernel<EPI, NT_STAGES, NT_KD>), dim3(p.tiles_m * p.tiles_n),
+                                           dim3(512), 0, s, p));
         return hipGetLastError();
     }
     return run<128, 128, 2, 2, false, false, EPI>(p, s);
@@ -813,7 +820,7 @@ hipError_t run_tn_big(GemmParams p, hipStream_t s) {
     p.tiles_n = (int)cdiv(p.N, BIG);
     const double work = 2.0 * p.M * p.N * (double)p.nk_total * BK;
     PROF_LAUNCH(gemm_class(true, EPI), work, s,
-                hipLaunchKernelGGL((gemm_tn_pipe_kernel<EPI, NT_STAGES>), dim3(p.tiles_m * p.tiles_n * p.splits),
+                hipLaunchKernelGGL((gemm_tn_pipe_kernel<EPI, TN_STAGES>), dim3(p.tiles_m * p.tiles_n * p.splits),
                                    dim3(256), 0, s, p));
     return hipGetLastError();
 }
