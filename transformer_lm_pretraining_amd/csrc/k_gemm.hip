@@ -10,7 +10,7 @@
 //     are read transposed out of LDS (ds_read_b64_tr_b16).  The bias gradient
 //     (column sums of dY) is folded into the same pass: the workgroups of the
 //     first output column tile sum the dY fragments they read anyway.
-// Large problems run 256x256 tiles (gemm_nt_w8_kernel, gemm_tn_pipe_kernel):
+// Large problems run 256x256 tiles (gemm_nt_w8_kernel, gemm_tn_w8_kernel):
 // operands go global -> LDS without register staging, several stages in
 // flight.  Small ones run the generic BM x BN kernel (gemm_kernel: register
 // prefetch, LDS double buffer, rows padded to 72 bf16).  Workgroups are
@@ -294,6 +294,9 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* src, uint16_t* dst_wav
 #ifndef TN_STAGES
 #define TN_STAGES 4
 #endif
+#ifndef TN_TD
+#define TN_TD 32
+#endif
 constexpr int PBK = 32;                  // reduction depth of one stage
 constexpr int PSTAGE = 2 * BIG * PBK;    // A and B tiles of one stage, bf16 elements (32 KB)
 
@@ -545,10 +548,11 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_w8_kernel(GemmParams p) {
 
 // ---------------------------------------------------------------------------
 // Pipelined TN tiles (weight gradients): dW[r][c] (+)= sum_t dY[t][r] X[t][c]
-// over one split's token range, 256x256 output tile, four 128x128 wave tiles.
-// Both operands are token-major, so a stage holds 32 tokens x 256 features of
-// each, loaded straight into LDS (global_load_lds_dwordx4: 1 KB = 2 token
-// rows of 512 B per wave instruction) with the 16-byte vector v of row t at
+// over one split's token range, 256x256 output tile per workgroup of eight
+// waves (wave grid 2 x 4 of 128x64 wave tiles, as for NT).  Both operands are
+// token-major, so a stage holds TD tokens x 256 features of each, loaded
+// straight into LDS (global_load_lds_dwordx4: 1 KB = 2 token rows of 512 B
+// per wave instruction) with the 16-byte vector v of row t at
 // slot v ^ ((t & 7) << 2).  The MFMA fragments are the transposes of those
 // tiles, read with ds_read_b64_tr_b16 (8 consecutive tokens of one feature
 // per lane); the XOR spreads the 8 token rows one read touches over the banks.
@@ -558,7 +562,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_w8_kernel(GemmParams p) {
 // bias gradient).  The fp32 epilogue goes through a per-wave LDS buffer so
 // each row segment is written (or read-modified-written) in 512-byte runs.
 
-// LDS element offset of (token t, feature f) within a 32 x 256 stage tile.
+// LDS element offset of (token t, feature f) within a token-major stage tile.
 __device__ __forceinline__ int tn_off(int t, int f) { return t * BIG + (((f >> 3) ^ ((t & 7) << 2)) << 3) + (f & 7); }
 
 typedef short tn_v4s __attribute__((ext_vector_type(4)));
@@ -580,190 +584,12 @@ __device__ __forceinline__ void lds_dma16_asm(const uint16_t* src, uint16_t* dst
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
 }
 
-template <int EPI, int NS>
-__global__ __launch_bounds__(256, 1) void gemm_tn_pipe_kernel(GemmParams p) {
-    static_assert(NS >= 2 && NS <= 5, "stage count");
-    __shared__ __attribute__((aligned(16))) uint16_t smem[NS * PSTAGE];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
-    const int wm = wave >> 1, wn = wave & 1;
-
-    const int ntiles = p.tiles_m * p.tiles_n;
-    const int total = ntiles * p.splits;
-    int lin = blockIdx.x;
-    if ((total % NUM_XCD) == 0) lin = (lin % NUM_XCD) * (total / NUM_XCD) + lin / NUM_XCD;
-    const int split = lin / ntiles;
-    const int pid = lin % ntiles;
-    const int in_group = GROUP_M * p.tiles_n;
-    const int first_m = (pid / in_group) * GROUP_M;
-    const int gsize = min(p.tiles_m - first_m, GROUP_M);
-    const int tm = first_m + (pid % in_group) % gsize;
-    const int tn = (pid % in_group) / gsize;
-    const int m0 = tm * BIG, n0 = tn * BIG;  // dY feature (output row) and X feature (output column) origins
-    const int steps = p.nk_total * (BK / PBK);
-    const int q = steps / p.splits, rr = steps % p.splits;
-    const int nk = q + (split < rr ? 1 : 0);                 // >= 1: the host keeps splits <= steps
-    const int tok0 = (split * q + min(split, rr)) * PBK;
-    const bool sum_rows = p.dbias != nullptr && tn == 0 && wn == 0;
-
-    // Load instruction i of this wave covers token rows 8*wave + 2*i + (lane>>5) of
-    // the stage, physical vector lane&31, i.e. logical vector (lane&31) ^ ((row&7)<<2).
-    // Features past M / N are clamped (their products are never stored).
-    uint32_t offA[4], offB[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 8 * wave + 2 * i + g;
-        const int lv = (lane & 31) ^ ((row & 7) << 2);
-        offA[i] = (uint32_t)(tok0 + row) * (uint32_t)p.lda + (uint32_t)min(m0 + lv * 8, p.M - 8);
-        offB[i] = (uint32_t)(tok0 + row) * (uint32_t)p.ldb + (uint32_t)min(n0 + lv * 8, p.N - 8);
-    }
-    const uint32_t stepA = (uint32_t)PBK * (uint32_t)p.lda, stepB = (uint32_t)PBK * (uint32_t)p.ldb;
-    auto issue = [&](int t) {
-        uint16_t* sa = smem + (t % NS) * PSTAGE;
-        uint16_t* sb = sa + PBK * BIG;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            lds_dma16_asm(p.A + (offA[i] + (uint32_t)t * stepA), sa + (8 * wave + 2 * i) * BIG);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            lds_dma16_asm(p.B + (offB[i] + (uint32_t)t * stepB), sb + (8 * wave + 2 * i) * BIG);
-    };
-
-#pragma unroll
-    for (int t = 0; t < NS; ++t)
-        if (t < nk) issue(t);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // acc[i][j][4*rg + e] is dW[m0 + wm*128 + i*32 + (lane&31)][n0 + wn*128 + j*32 + 8*rg + 4*g + e]
-    floatx16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    float bsum[4] = {0.f, 0.f, 0.f, 0.f};
-    wait_stage_groups<8>(min(NS, nk) - 1);
-    __syncthreads();
-
-    // per-lane fragment addresses within a stage tile (token row 4g + (lane&15)/4,
-    // features col0 + 16*((lane>>4)&1) + 4*(lane&3), col0 = 32-column subtile)
-    int fa[4], fb[4];
-    {
-        const int t = 4 * g + ((lane & 15) >> 2);
-        const int f = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            fa[i] = tn_off(t, wm * 128 + i * 32 + f);
-            fb[i] = PBK * BIG + tn_off(t, wn * 128 + i * 32 + f);
-        }
-    }
-    bf16x8 dyf[2][4], xf[2][4];
-    auto read_frags = [&](const uint16_t* st, int ks, int b) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dyf[b][i] = tn_frag(st + fa[i] + ks * 16 * BIG);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xf[b][j] = tn_frag(st + fb[j] + ks * 16 * BIG);
-    };
-    auto add_bias = [&](int b) {
-        if (sum_rows) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x4 w = __builtin_bit_cast(u32x4, dyf[b][i]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) bsum[i] += bflo(w[e]) + bfhi(w[e]);
-            }
-        }
-    };
-    read_frags(smem, 0, 0);
-    int s = 0;
-    do {
-        const uint16_t* st = smem + (s % NS) * PSTAGE;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(xf[0][j], dyf[0][i], acc[i][j]);
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(st, 1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 2; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(xf[0][j], dyf[0][i], acc[i][j]);
-        add_bias(0);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(xf[1][j], dyf[1][i], acc[i][j]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (s + 1 < nk) {
-            wait_stage_groups<8>(min(s + NS - 1, nk - 1) - (s + 1));
-            __syncthreads();
-            // all of stage s is in registers: its buffer takes stage s+NS
-            if (s + NS < nk) issue(s + NS);
-            read_frags(smem + ((s + 1) % NS) * PSTAGE, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 2; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(xf[1][j], dyf[1][i], acc[i][j]);
-        add_bias(1);
-        __builtin_amdgcn_sched_barrier(0);
-    } while (++s < nk);
-    __syncthreads();
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-
-    if (sum_rows) {
-        // the two lane halves hold different tokens of the same feature rows
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float t = bsum[i] + __shfl_xor(bsum[i], 32, WAVE);
-            const int row = m0 + wm * 128 + i * 32 + (lane & 31);
-            if (g == 0 && row < p.M) unsafeAtomicAdd(p.dbias + row, t);
-        }
-    }
-
-    // Epilogue through a per-wave 32 x 128 fp32 buffer (16 KB), one 32-row group i
-    // at a time: 16-byte vector v of buffer row r sits at slot v ^ r.
-    float* buf = (float*)smem + wave * (32 * 128);
-    const int fr = lane & 31;
-    float* outp = EPI == EPI_F32_ACC ? p.outf : p.outf + split * p.split_stride;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int v = 8 * j + 2 * rg + g;  // 16-byte vector index within the 128-column row
-                *(float4*)(buf + fr * 128 + ((v ^ fr) << 2)) =
-                    make_float4(acc_read(acc[i][j][4 * rg]), acc_read(acc[i][j][4 * rg + 1]),
-                                acc_read(acc[i][j][4 * rg + 2]), acc_read(acc[i][j][4 * rg + 3]));
-            }
-        // read back row-contiguous: lane covers vector lane&31 of rows 2*it + g
-#pragma unroll 4
-        for (int it = 0; it < 16; ++it) {
-            const int r = 2 * it + g, v = lane & 31;
-            const float4 a = *(const float4*)(buf + r * 128 + ((v ^ r) << 2));
-            const int row = m0 + wm * 128 + i * 32 + r, col = n0 + wn * 128 + v * 4;
-            if (row < p.M && col < p.N) {
-                float4* o = (float4*)(outp + (int64_t)row * p.ldf + col);
-                if constexpr (EPI == EPI_F32_ACC) {
-                    float4 c = *o;
-                    c.x += a.x; c.y += a.y; c.z += a.z; c.w += a.w;
-                    *o = c;
-                } else {
-                    *o = a;
-                }
-            }
-        }
-    }
-}
-
-template <int EPI, int NS>
+template <int EPI, int NS, int TD>
 __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(GemmParams p) {
-    static_assert(NS >= 2 && NS <= 5, "stage count");
-    __shared__ __attribute__((aligned(16))) uint16_t smem[NS * PSTAGE];
+    // a stage holds TD tokens of both operands; each wave issues IPO 1 KB loads per operand
+    constexpr int SE = 2 * TD * BIG, IPO = TD / 16, KS = TD / 16;
+    static_assert(NS >= 2 && NS * SE * 2 <= 160 * 1024 && NS * SE >= 8 * 32 * 64 * 2, "stage count");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NS * SE];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
     const int wm = wave >> 2, wn = wave & 3;
 
@@ -779,33 +605,33 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(GemmParams p) {
     const int tm = first_m + (pid % in_group) % gsize;
     const int tn = (pid % in_group) / gsize;
     const int m0 = tm * BIG, n0 = tn * BIG;  // dY feature (output row) and X feature (output column) origins
-    const int steps = p.nk_total * (BK / PBK);
+    const int steps = p.nk_total * (BK / TD);
     const int q = steps / p.splits, rr = steps % p.splits;
     const int nk = q + (split < rr ? 1 : 0);                 // >= 1: the host keeps splits <= steps
-    const int tok0 = (split * q + min(split, rr)) * PBK;
+    const int tok0 = (split * q + min(split, rr)) * TD;
     const bool sum_rows = p.dbias != nullptr && tn == 0 && wn == 0;
 
-    // Load instruction i of this wave covers token rows 4*wave + 2*i + (lane>>5) of
-    // the stage, physical vector lane&31, i.e. logical vector (lane&31) ^ ((row&7)<<2).
+    // Load instruction i of this wave covers token rows 2*(wave*IPO + i) + (lane>>5)
+    // of the stage, physical vector lane&31, i.e. logical vector (lane&31) ^ ((row&7)<<2).
     // Features past M / N are clamped (their products are never stored).
-    uint32_t offA[2], offB[2];
+    uint32_t offA[IPO], offB[IPO];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = 4 * wave + 2 * i + g;
+    for (int i = 0; i < IPO; ++i) {
+        const int row = 2 * (wave * IPO + i) + g;
         const int lv = (lane & 31) ^ ((row & 7) << 2);
         offA[i] = (uint32_t)(tok0 + row) * (uint32_t)p.lda + (uint32_t)min(m0 + lv * 8, p.M - 8);
         offB[i] = (uint32_t)(tok0 + row) * (uint32_t)p.ldb + (uint32_t)min(n0 + lv * 8, p.N - 8);
     }
-    const uint32_t stepA = (uint32_t)PBK * (uint32_t)p.lda, stepB = (uint32_t)PBK * (uint32_t)p.ldb;
+    const uint32_t stepA = (uint32_t)TD * (uint32_t)p.lda, stepB = (uint32_t)TD * (uint32_t)p.ldb;
     auto issue = [&](int t) {
-        uint16_t* sa = smem + (t % NS) * PSTAGE;
-        uint16_t* sb = sa + PBK * BIG;
+        uint16_t* sa = smem + (t % NS) * SE;
+        uint16_t* sb = sa + TD * BIG;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            lds_dma16_asm(p.A + (offA[i] + (uint32_t)t * stepA), sa + (4 * wave + 2 * i) * BIG);
+        for (int i = 0; i < IPO; ++i)
+            lds_dma16_asm(p.A + (offA[i] + (uint32_t)t * stepA), sa + 2 * (wave * IPO + i) * BIG);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            lds_dma16_asm(p.B + (offB[i] + (uint32_t)t * stepB), sb + (4 * wave + 2 * i) * BIG);
+        for (int i = 0; i < IPO; ++i)
+            lds_dma16_asm(p.B + (offB[i] + (uint32_t)t * stepB), sb + 2 * (wave * IPO + i) * BIG);
     };
 
 #pragma unroll
@@ -822,7 +648,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(GemmParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     float bsum[4] = {0.f, 0.f, 0.f, 0.f};
-    wait_stage_groups<4>(min(NS, nk) - 1);
+    wait_stage_groups<2 * IPO>(min(NS, nk) - 1);
     __syncthreads();
 
     // per-lane fragment addresses within a stage tile (token row 4g + (lane&15)/4,
@@ -834,7 +660,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(GemmParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) fa[i] = tn_off(t, wm * 128 + i * 32 + f);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) fb[j] = PBK * BIG + tn_off(t, wn * 64 + j * 32 + f);
+        for (int j = 0; j < 2; ++j) fb[j] = TD * BIG + tn_off(t, wn * 64 + j * 32 + f);
     }
     bf16x8 dyf[2][4], xf[2][2];
     auto read_frags = [&](const uint16_t* st, int ks, int b) {
@@ -853,42 +679,35 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(GemmParams p) {
             }
         }
     };
+    auto mma = [&](int b, int i0) {
+#pragma unroll
+        for (int i = i0; i < i0 + 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(xf[b][j], dyf[b][i], acc[i][j]);
+    };
     read_frags(smem, 0, 0);
     int s = 0;
     do {
-        const uint16_t* st = smem + (s % NS) * PSTAGE;
+        const uint16_t* st = smem + (s % NS) * SE;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(xf[0][j], dyf[0][i], acc[i][j]);
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(st, 1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 2; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(xf[0][j], dyf[0][i], acc[i][j]);
-        add_bias(0);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(xf[1][j], dyf[1][i], acc[i][j]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (s + 1 < nk) {
-            wait_stage_groups<4>(min(s + NS - 1, nk - 1) - (s + 1));
-            __syncthreads();
-            // all of stage s is in registers: its buffer takes stage s+NS
-            if (s + NS < nk) issue(s + NS);
-            read_frags(smem + ((s + 1) % NS) * PSTAGE, 0, 0);
+        for (int kk = 0; kk < KS; ++kk) {
+            const int b = kk & 1;
+            mma(b, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kk + 1 < KS) {
+                read_frags(st, kk + 1, b ^ 1);
+            } else if (s + 1 < nk) {
+                wait_stage_groups<2 * IPO>(min(s + NS - 1, nk - 1) - (s + 1));
+                __syncthreads();
+                // all of stage s is in registers: its buffer takes stage s+NS
+                if (s + NS < nk) issue(s + NS);
+                read_frags(smem + ((s + 1) % NS) * SE, 0, b ^ 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            mma(b, 2);
+            add_bias(b);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 2; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(xf[1][j], dyf[1][i], acc[i][j]);
-        add_bias(1);
-        __builtin_amdgcn_sched_barrier(0);
     } while (++s < nk);
     __syncthreads();
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -969,7 +788,7 @@ hipError_t run(GemmParams p, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Forward / input-gradient products: 256x256 tiles (four 128x128 wave tiles)
+// Forward / input-gradient products: 256x256 tiles (eight 128x64 wave tiles)
 // when the problem has enough of them, else 128x128.
 template <int EPI>
 hipError_t run_nt(GemmParams p, hipStream_t s) {
@@ -999,7 +818,7 @@ hipError_t run_tn_big(GemmParams p, hipStream_t s) {
     p.tiles_n = (int)cdiv(p.N, BIG);
     const double work = 2.0 * p.M * p.N * (double)p.nk_total * BK;
     PROF_LAUNCH(gemm_class(true, EPI), work, s,
-                hipLaunchKernelGGL((gemm_tn_w8_kernel<EPI, TN_STAGES>), dim3(p.tiles_m * p.tiles_n * p.splits),
+                hipLaunchKernelGGL((gemm_tn_w8_kernel<EPI, TN_STAGES, TN_TD>), dim3(p.tiles_m * p.tiles_n * p.splits),
                                    dim3(512), 0, s, p));
     return hipGetLastError();
 }
