@@ -90,7 +90,7 @@ struct LayerActs {
 struct ActsPlan {
     std::vector<LayerActs> layer;
     int64_t xfinal, lnf, meanf, rstdf, logits, loss_rows;
-    int64_t d_res, d_ln, d_big, d_qkv, d_att;
+    int64_t d_res[3], d_ln, d_big, d_qkv, d_att;
     int64_t total;
 };
 struct ScratchPlan {
@@ -132,7 +132,7 @@ ActsPlan plan_acts(const gpt2_config& c) {
     a.rstdf = take(BT * 4);
     a.logits = take(BT * (int64_t)c.Vp * 2);
     a.loss_rows = take(BT * 4);
-    a.d_res = take(BT * C * 2);
+    for (int i = 0; i < 3; ++i) a.d_res[i] = take(BT * C * 2);
     a.d_ln = take(BT * C * 2);
     a.d_big = take(BT * 4 * C * 2);
     a.d_qkv = take(BT * 3 * C * 2);
@@ -155,11 +155,15 @@ ScratchPlan plan_scratch(const gpt2_config& c) {
                                     colsum_partial_elems(BT, 3 * c.C)});
     s.col_partial = off;
     off = align_up(off + s.col_partial_elems * 4);
-    s.splitk_elems = std::max({gemm_tn_partial_elems((int)BT, 3 * (int)C, (int)C),
-                               gemm_tn_partial_elems((int)BT, (int)C, (int)C),
-                               gemm_tn_partial_elems((int)BT, 4 * (int)C, (int)C),
-                               gemm_tn_partial_elems((int)BT, (int)C, 4 * (int)C),
-                               gemm_tn_partial_elems((int)BT, c.Vp, (int)C)});
+    {
+        // one block's grouped weight-gradient products, and the lm_head's
+        const TnJobDesc blk[4] = {{nullptr, C, nullptr, 4 * C, (int)C, 4 * (int)C, nullptr, nullptr},
+                                  {nullptr, 4 * C, nullptr, C, 4 * (int)C, (int)C, nullptr, nullptr},
+                                  {nullptr, C, nullptr, C, (int)C, (int)C, nullptr, nullptr},
+                                  {nullptr, 3 * C, nullptr, C, 3 * (int)C, (int)C, nullptr, nullptr}};
+        s.splitk_elems = std::max(gemm_tn_group_partial_elems(blk, 4, (int)BT),
+                                  gemm_tn_partial_elems((int)BT, c.Vp, (int)C));
+    }
     s.splitk = off;
     off = align_up(off + s.splitk_elems * 4);
     s.dvec = off;
@@ -307,6 +311,27 @@ int run_forward(gpt2_handle* h, const int32_t* tok, const int32_t* tgt, float dl
     return GPT2_OK;
 }
 
+// The four weight-gradient products of block l, one grouped launch (run once
+// the block's input gradient is done, so their dY tensors are all still held:
+// the residual-stream gradients at the block output and at x_mid, dpre, dqkv).
+TnJobDesc block_dw_job(gpt2_handle* h, int l, int which, const uint16_t* d_out, const uint16_t* d_mid) {
+    const gpt2_config& c = h->cfg;
+    const int C = c.C;
+    const LayerActs& la = h->acts.layer[l];
+    switch (which) {
+        case 0:  // FC-proj: x_next = x_mid + gel . W_fp^T + b_fp
+            return {d_out, C, h->act<uint16_t>(la.gel), 4 * C, C, 4 * C, h->G(h->i_mat(l, 3)), h->G(h->i_vec(l, 7))};
+        case 1:  // FC: pre = ln2 . W_fc^T + b_fc
+            return {h->act<uint16_t>(h->acts.d_big), 4 * C, h->act<uint16_t>(la.ln2), C, 4 * C, C, h->G(h->i_mat(l, 2)),
+                    h->G(h->i_vec(l, 6))};
+        case 2:  // attention projection: x_mid = x + att . W_p^T + b_p
+            return {d_mid, C, h->act<uint16_t>(la.att), C, C, C, h->G(h->i_mat(l, 1)), h->G(h->i_vec(l, 3))};
+        default:  // QKV: qkv = ln1 . W_qkv^T + b_qkv
+            return {h->act<uint16_t>(h->acts.d_qkv), 3 * C, h->act<uint16_t>(la.ln1), C, 3 * C, C,
+                    h->G(h->i_mat(l, 0)), h->G(h->i_vec(l, 2))};
+    }
+}
+
 int run_backward(gpt2_handle* h, hipStream_t s) {
     const gpt2_config& c = h->cfg;
     const int BT = c.B * c.T, C = c.C;
@@ -314,7 +339,9 @@ int run_backward(gpt2_handle* h, hipStream_t s) {
     float* colp = (float*)(h->S() + h->scr.col_partial);
     float* splitk = (float*)(h->S() + h->scr.splitk);
     const int64_t splitk_n = h->scr.splitk_elems;
-    uint16_t* d_res = h->act<uint16_t>(A.d_res);
+    // residual-stream gradients rotate through three buffers: a block reads the one
+    // at its output, writes the one at x_mid and the one at its input
+    uint16_t* d_res[3] = {h->act<uint16_t>(A.d_res[0]), h->act<uint16_t>(A.d_res[1]), h->act<uint16_t>(A.d_res[2])};
     uint16_t* d_ln = h->act<uint16_t>(A.d_ln);
     uint16_t* d_big = h->act<uint16_t>(A.d_big);
     uint16_t* d_qkv = h->act<uint16_t>(A.d_qkv);
@@ -325,42 +352,42 @@ int run_backward(gpt2_handle* h, hipStream_t s) {
     HIPCHK(launch_gemm_nt(dlogits, c.Vp, h->WT(h->i_wte()), c.Vp, BT, C, c.Vp, nullptr, nullptr, 0, d_ln, C, s));
     HIPCHK(launch_gemm_tn_acc(dlogits, c.Vp, h->act<uint16_t>(A.lnf), C, BT, c.Vp, C, h->G(h->i_wte()), nullptr,
                               splitk, splitk_n, s));
+    int ri = 0;
     HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(A.xfinal), d_ln, h->P(h->i_lnf(0)), h->act<float>(A.meanf),
-                                h->act<float>(A.rstdf), d_res, 0, h->G(h->i_lnf(0)), h->G(h->i_lnf(1)), colp, BT, C,
-                                s));
+                                h->act<float>(A.rstdf), d_res[ri], d_res[ri], 0, h->G(h->i_lnf(0)),
+                                h->G(h->i_lnf(1)), colp, BT, C, s));
     for (int l = c.L - 1; l >= 0; --l) {
         const LayerActs& la = A.layer[l];
-        // FC-proj: x_next = x_mid + gel . W_fp^T + b_fp.  The input gradient is taken
-        // through GELU in the GEMM epilogue (d_big = dpre); b_fp's gradient rides on the dW pass.
-        HIPCHK(launch_gemm_nt_dgelu(d_res, C, h->WT(h->i_mat(l, 3)), C, BT, 4 * C, C, h->act<uint16_t>(la.pre), d_big,
+        uint16_t* d_out = d_res[ri];            // gradient at the block output
+        uint16_t* d_mid = d_res[(ri + 1) % 3];  // at x_mid
+        uint16_t* d_in = d_res[(ri + 2) % 3];   // at the block input
+        // FC-proj input gradient, taken through GELU in the epilogue: d_big = dpre
+        HIPCHK(launch_gemm_nt_dgelu(d_out, C, h->WT(h->i_mat(l, 3)), C, BT, 4 * C, C, h->act<uint16_t>(la.pre), d_big,
                                     4 * C, s));
-        HIPCHK(launch_gemm_tn_acc(d_res, C, h->act<uint16_t>(la.gel), 4 * C, BT, C, 4 * C, h->G(h->i_mat(l, 3)),
-                                  h->G(h->i_vec(l, 7)), splitk, splitk_n, s));
-        // FC: pre = ln2 . W_fc^T + b_fc
+        // FC input gradient, then LN2: d_mid = d_out + LN2'(d_ln)
         HIPCHK(launch_gemm_nt(d_big, 4 * C, h->WT(h->i_mat(l, 2)), 4 * C, BT, C, 4 * C, nullptr, nullptr, 0, d_ln, C,
                               s));
-        HIPCHK(launch_gemm_tn_acc(d_big, 4 * C, h->act<uint16_t>(la.ln2), C, BT, 4 * C, C, h->G(h->i_mat(l, 2)),
-                                  h->G(h->i_vec(l, 6)), splitk, splitk_n, s));
         HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(la.xmid), d_ln, h->P(h->i_vec(l, 4)), h->act<float>(la.mean2),
-                                    h->act<float>(la.rstd2), d_res, 1, h->G(h->i_vec(l, 4)), h->G(h->i_vec(l, 5)),
-                                    colp, BT, C, s));
-        // attention projection: x_mid = x + att . W_p^T + b_p
-        HIPCHK(launch_gemm_nt(d_res, C, h->WT(h->i_mat(l, 1)), C, BT, C, C, nullptr, nullptr, 0, d_att, C, s));
-        HIPCHK(launch_gemm_tn_acc(d_res, C, h->act<uint16_t>(la.att), C, BT, C, C, h->G(h->i_mat(l, 1)),
-                                  h->G(h->i_vec(l, 3)), splitk, splitk_n, s));
+                                    h->act<float>(la.rstd2), d_out, d_mid, 1, h->G(h->i_vec(l, 4)),
+                                    h->G(h->i_vec(l, 5)), colp, BT, C, s));
+        // attention projection input gradient, attention, QKV input gradient
+        HIPCHK(launch_gemm_nt(d_mid, C, h->WT(h->i_mat(l, 1)), C, BT, C, C, nullptr, nullptr, 0, d_att, C, s));
         HIPCHK(launch_attention_bwd(h->act<uint16_t>(la.qkv), h->act<uint16_t>(la.att), d_att,
                                     h->act<float>(la.lse), d_qkv, (float*)(h->S() + h->scr.dvec), c.B, c.T, c.H, C,
                                     s));
-        // QKV: qkv = ln1 . W_qkv^T + b_qkv
         HIPCHK(launch_gemm_nt(d_qkv, 3 * C, h->WT(h->i_mat(l, 0)), 3 * C, BT, C, 3 * C, nullptr, nullptr, 0, d_ln, C,
                               s));
-        HIPCHK(launch_gemm_tn_acc(d_qkv, 3 * C, h->act<uint16_t>(la.ln1), C, BT, 3 * C, C, h->G(h->i_mat(l, 0)),
-                                  h->G(h->i_vec(l, 2)), splitk, splitk_n, s));
+        // LN1: d_in = d_mid + LN1'(d_ln)
         HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(la.x), d_ln, h->P(h->i_vec(l, 0)), h->act<float>(la.mean1),
-                                    h->act<float>(la.rstd1), d_res, 1, h->G(h->i_vec(l, 0)), h->G(h->i_vec(l, 1)),
-                                    colp, BT, C, s));
+                                    h->act<float>(la.rstd1), d_mid, d_in, 1, h->G(h->i_vec(l, 0)),
+                                    h->G(h->i_vec(l, 1)), colp, BT, C, s));
+        // the block's weight and bias gradients
+        TnJobDesc jobs[4];
+        for (int k = 0; k < 4; ++k) jobs[k] = block_dw_job(h, l, k, d_out, d_mid);
+        HIPCHK(launch_gemm_tn_group(jobs, 4, BT, splitk, splitk_n, s));
+        ri = (ri + 2) % 3;
     }
-    HIPCHK(launch_embedding_bwd(h->last_tok, d_res, h->G(h->i_wte()), h->G(h->i_wpe()), c.B, c.T, C, c.V,
+    HIPCHK(launch_embedding_bwd(h->last_tok, d_res[ri], h->G(h->i_wte()), h->G(h->i_wpe()), c.B, c.T, C, c.V,
                                 (int32_t*)(h->S() + h->scr.emb_work), h->scr.emb_work_elems, s));
     return GPT2_OK;
 }
@@ -654,7 +681,7 @@ int gpt2k_layernorm_bwd(const uint16_t* x, const uint16_t* dy, const float* w, c
     if (!x || !dy || !w || !mean || !rstd || !dres || !dw || !db || !scratch || rows < 0) return GPT2_E_INVALID;
     if (!layernorm_supports(C)) return GPT2_E_SHAPE;
     if (scratch_bytes < layernorm_bwd_partial_elems(rows, C) * 4) return GPT2_E_INVALID;
-    KCHK(launch_layernorm_bwd(x, dy, w, mean, rstd, dres, accumulate, dw, db, (float*)scratch, rows, C, s));
+    KCHK(launch_layernorm_bwd(x, dy, w, mean, rstd, dres, dres, accumulate, dw, db, (float*)scratch, rows, C, s));
     return GPT2_OK;
 }
 

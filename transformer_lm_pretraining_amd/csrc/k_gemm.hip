@@ -584,8 +584,23 @@ __device__ __forceinline__ void lds_dma16_asm(const uint16_t* src, uint16_t* dst
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
 }
 
+// One weight-gradient product of a grouped launch.
+constexpr int TN_MAX_JOBS = 4;
+struct TnJob {
+    const uint16_t* A;  // dY [tokens][M] (row stride lda)
+    const uint16_t* B;  // X  [tokens][N] (row stride ldb)
+    int lda, ldb, M, N, tiles_m, tiles_n;
+    float* out;         // dW [M][N] (EPI_F32_ACC) or split partials, split s at out + s * M * N
+    float* dbias;       // += column sums of dY (may be null)
+};
+struct TnGroup {
+    TnJob job[TN_MAX_JOBS];
+    int tile_start[TN_MAX_JOBS + 1];  // prefix sums of the jobs' tile counts
+    int njobs, splits, nk_total;      // nk_total = tokens / 64
+};
+
 template <int EPI, int NS, int TD>
-__global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(GemmParams p) {
+__global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(TnGroup G) {
     // a stage holds TD tokens of both operands; each wave issues IPO 1 KB loads per operand
     constexpr int SE = 2 * TD * BIG, IPO = TD / 16, KS = TD / 16;
     static_assert(NS >= 2 && NS * SE * 2 <= 160 * 1024 && NS * SE >= 8 * 32 * 64 * 2, "stage count");
@@ -593,20 +608,23 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(GemmParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
     const int wm = wave >> 2, wn = wave & 3;
 
-    const int ntiles = p.tiles_m * p.tiles_n;
-    const int total = ntiles * p.splits;
+    const int ntiles = G.tile_start[G.njobs];
+    const int total = ntiles * G.splits;
     int lin = blockIdx.x;
     if ((total % NUM_XCD) == 0) lin = (lin % NUM_XCD) * (total / NUM_XCD) + lin / NUM_XCD;
     const int split = lin / ntiles;
-    const int pid = lin % ntiles;
+    int pid = lin % ntiles, jb = 0;
+    while (jb + 1 < G.njobs && pid >= G.tile_start[jb + 1]) ++jb;
+    pid -= G.tile_start[jb];
+    const TnJob p = G.job[jb];
     const int in_group = GROUP_M * p.tiles_n;
     const int first_m = (pid / in_group) * GROUP_M;
     const int gsize = min(p.tiles_m - first_m, GROUP_M);
     const int tm = first_m + (pid % in_group) % gsize;
     const int tn = (pid % in_group) / gsize;
     const int m0 = tm * BIG, n0 = tn * BIG;  // dY feature (output row) and X feature (output column) origins
-    const int steps = p.nk_total * (BK / TD);
-    const int q = steps / p.splits, rr = steps % p.splits;
+    const int steps = G.nk_total * (BK / TD);
+    const int q = steps / G.splits, rr = steps % G.splits;
     const int nk = q + (split < rr ? 1 : 0);                 // >= 1: the host keeps splits <= steps
     const int tok0 = (split * q + min(split, rr)) * TD;
     const bool sum_rows = p.dbias != nullptr && tn == 0 && wn == 0;
@@ -726,7 +744,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(GemmParams p) {
     // at a time: 16-byte vector v of buffer row r sits at slot v ^ (r & 15).
     float* buf = (float*)smem + wave * (32 * 64);
     const int fr = lane & 31;
-    float* outp = EPI == EPI_F32_ACC ? p.outf : p.outf + split * p.split_stride;
+    float* outp = EPI == EPI_F32_ACC ? p.out : p.out + (int64_t)split * p.M * p.N;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -745,7 +763,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(GemmParams p) {
             const float4 a = *(const float4*)(buf + r * 64 + ((v ^ (r & 15)) << 2));
             const int row = m0 + wm * 128 + i * 32 + r, col = n0 + wn * 64 + v * 4;
             if (row < p.M && col < p.N) {
-                float4* o = (float4*)(outp + (int64_t)row * p.ldf + col);
+                float4* o = (float4*)(outp + (int64_t)row * p.N + col);
                 if constexpr (EPI == EPI_F32_ACC) {
                     float4 c = *o;
                     c.x += a.x; c.y += a.y; c.z += a.z; c.w += a.w;
@@ -768,6 +786,29 @@ __global__ void splitk_reduce_kernel(const float4* __restrict__ part, float4* __
             a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
         }
         dw[i] = a;
+    }
+}
+
+// dW_j += sum over splits of job j's partials, all jobs of a group in one launch
+// (float4 vectors; job j owns vectors [start4[j], start4[j+1]) of the index space).
+struct TnReduce {
+    const float4* part[TN_MAX_JOBS];
+    float4* dw[TN_MAX_JOBS];
+    int64_t start4[TN_MAX_JOBS + 1];
+    int njobs, splits;
+};
+__global__ void splitk_reduce_group_kernel(TnReduce R) {
+    const int64_t n4 = R.start4[R.njobs];
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+        int j = 0;
+        while (j + 1 < R.njobs && i >= R.start4[j + 1]) ++j;
+        const int64_t e = i - R.start4[j], stride4 = R.start4[j + 1] - R.start4[j];
+        float4 a = R.dw[j][e];
+        for (int sp = 0; sp < R.splits; ++sp) {
+            const float4 b = R.part[j][sp * stride4 + e];
+            a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+        }
+        R.dw[j][e] = a;
     }
 }
 
@@ -812,40 +853,84 @@ hipError_t run_nt(GemmParams p, hipStream_t s) {
     return run<128, 128, 2, 2, false, false, EPI>(p, s);
 }
 
-template <int EPI>
-hipError_t run_tn_big(GemmParams p, hipStream_t s) {
-    p.tiles_m = (int)cdiv(p.M, BIG);
-    p.tiles_n = (int)cdiv(p.N, BIG);
-    const double work = 2.0 * p.M * p.N * (double)p.nk_total * BK;
-    PROF_LAUNCH(gemm_class(true, EPI), work, s,
-                hipLaunchKernelGGL((gemm_tn_w8_kernel<EPI, TN_STAGES, TN_TD>), dim3(p.tiles_m * p.tiles_n * p.splits),
-                                   dim3(512), 0, s, p));
-    return hipGetLastError();
-}
-
-// Weight-gradient split: a multiple of the tile count close to a whole number of
-// passes over the 256 CUs, each split keeping >= 4 K-steps.
-struct TnPlan {
-    int splits;
-    bool big;  // 256x256 tiles
-};
-TnPlan tn_plan(int M, int N, int K, bool pipe_ok = true) {
-    const int nk = M / BK;
-    const bool big = pipe_ok && (int64_t)cdiv(N, 256) * cdiv(K, 256) >= 8;
-    const int64_t tiles = big ? cdiv(N, 256) * cdiv(K, 256) : cdiv(N, 128) * cdiv(K, 128);
-    if (tiles >= NUM_CU) return {1, big};
+// Splits for a group of weight-gradient products with `tiles` 256x256 output
+// tiles in all: the fewest that fill at least 80% of the last pass over the 256
+// CUs (fewer splits, less partial traffic), else the best filling count; each
+// split keeps >= 4 K-steps of 64 tokens.
+int tn_group_splits(int64_t tiles, int nk) {
+    if (tiles >= NUM_CU) return 1;
     int best = 1;
     double best_eff = 0.0;
-    for (int s = 1; s <= 64 && nk / s >= 4; ++s) {
-        const int64_t wg = tiles * s;
-        const double waves = (double)wg / NUM_CU;
+    for (int sp = 1; sp <= 64 && nk / sp >= 4; ++sp) {
+        const double waves = (double)(tiles * sp) / NUM_CU;
         const double eff = waves / std::ceil(waves);
+        if (eff >= 0.8) return sp;
         if (eff > best_eff + 0.02) {
             best_eff = eff;
-            best = s;
+            best = sp;
         }
     }
-    return {best, big};
+    return best;
+}
+
+bool tn_pipe_ok(int M, int64_t ldy, int64_t ldx, int N, int K) {
+    // 32-bit element offsets, 16-byte vectors, 256x256 tiles worth running
+    return ldy % 8 == 0 && ldx % 8 == 0 && N % 8 == 0 && K % 8 == 0 && (int64_t)M * ldy < (1ll << 31) &&
+           (int64_t)M * ldx < (1ll << 31);
+}
+
+// Runs jobs [0, n) of equal token count M as one grouped 256x256-tile launch
+// (plus one reduce launch when split).
+hipError_t run_tn_group(const TnJobDesc* jobs, int n, int M, float* partial, int64_t partial_elems, hipStream_t s) {
+    TnGroup G{};
+    G.njobs = n;
+    G.nk_total = M / BK;
+    int64_t tiles = 0, elems = 0;
+    double work = 0.0;
+    for (int j = 0; j < n; ++j) {
+        const TnJobDesc& d = jobs[j];
+        TnJob& t = G.job[j];
+        t.A = d.dY; t.B = d.X; t.lda = (int)d.ldy; t.ldb = (int)d.ldx; t.M = d.N; t.N = d.K;
+        t.tiles_m = (int)cdiv(d.N, BIG); t.tiles_n = (int)cdiv(d.K, BIG);
+        t.dbias = d.db;
+        G.tile_start[j] = (int)tiles;
+        tiles += (int64_t)t.tiles_m * t.tiles_n;
+        elems += (int64_t)d.N * d.K;
+        work += 2.0 * d.N * d.K * (double)M;
+    }
+    G.tile_start[n] = (int)tiles;
+    int sp = tn_group_splits(tiles, G.nk_total);
+    if (sp > 1 && (partial == nullptr || partial_elems < sp * elems)) sp = 1;
+    G.splits = sp;
+    if (sp == 1) {
+        for (int j = 0; j < n; ++j) G.job[j].out = jobs[j].dW;
+        PROF_LAUNCH(KC_GEMM_TN_ACC, work, s,
+                    hipLaunchKernelGGL((gemm_tn_w8_kernel<EPI_F32_ACC, TN_STAGES, TN_TD>), dim3(tiles), dim3(512),
+                                       0, s, G));
+        return hipGetLastError();
+    }
+    TnReduce R{};
+    R.njobs = n;
+    R.splits = sp;
+    int64_t off = 0;
+    for (int j = 0; j < n; ++j) {
+        const int64_t e = (int64_t)jobs[j].N * jobs[j].K;
+        G.job[j].out = partial + off;
+        R.part[j] = (const float4*)(partial + off);
+        R.dw[j] = (float4*)jobs[j].dW;
+        R.start4[j + 1] = R.start4[j] + e / 4;
+        off += sp * e;
+    }
+    PROF_LAUNCH(KC_GEMM_TN_SPLIT, work, s,
+                hipLaunchKernelGGL((gemm_tn_w8_kernel<EPI_F32_STORE, TN_STAGES, TN_TD>), dim3(tiles * sp),
+                                   dim3(512), 0, s, G));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n4 = R.start4[n];
+    const int blocks = (int)std::min<int64_t>(cdiv(n4, 256), 4096);
+    PROF_LAUNCH(KC_SPLITK_REDUCE, 16.0 * n4 * (sp + 2), s,
+                hipLaunchKernelGGL(splitk_reduce_group_kernel, dim3(blocks), dim3(256), 0, s, R));
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -876,31 +961,45 @@ hipError_t launch_gemm_nt_dgelu(const uint16_t* A, int64_t lda, const uint16_t* 
 }
 
 int64_t gemm_tn_partial_elems(int M, int N, int K) {
-    TnPlan t = tn_plan(M, N, K);
-    return t.splits > 1 ? (int64_t)t.splits * N * K : 0;
+    const TnJobDesc d{nullptr, K, nullptr, K, N, K, nullptr, nullptr};
+    return gemm_tn_group_partial_elems(&d, 1, M);
 }
 
 hipError_t launch_gemm_tn_acc(const uint16_t* dY, int64_t ldy, const uint16_t* X, int64_t ldx, int M, int N, int K,
                               float* dW, float* dbias, float* partial, int64_t partial_elems, hipStream_t s) {
     // output rows = N (features of dY), output cols = K (features of X), reduction = M tokens
-    // the pipelined kernel addresses operands with 32-bit element offsets and 16-byte vectors
-    const bool pipe_ok = ldy % 8 == 0 && ldx % 8 == 0 && (int64_t)M * ldy < (1ll << 31) && (int64_t)M * ldx < (1ll << 31);
-    TnPlan t = tn_plan(M, N, K, pipe_ok);
-    if (t.splits > 1 && (partial == nullptr || partial_elems < (int64_t)t.splits * N * K)) t.splits = 1;
-    GemmParams p{};
-    p.A = dY; p.B = X; p.lda = ldy; p.ldb = ldx; p.M = N; p.N = K; p.nk_total = M / BK; p.splits = t.splits;
-    p.dbias = dbias;
-    if (t.splits == 1) {
-        p.outf = dW; p.ldf = K;
-        return t.big ? run_tn_big<EPI_F32_ACC>(p, s) : run<128, 128, 2, 2, true, true, EPI_F32_ACC>(p, s);
+    const TnJobDesc d{dY, ldy, X, ldx, N, K, dW, dbias};
+    return launch_gemm_tn_group(&d, 1, M, partial, partial_elems, s);
+}
+
+hipError_t launch_gemm_tn_group(const TnJobDesc* jobs, int n, int M, float* partial, int64_t partial_elems,
+                                hipStream_t s) {
+    if (n < 1 || n > TN_MAX_JOBS || M < BK || M % BK) return hipErrorInvalidValue;
+    int64_t tiles = 0;
+    bool pipe = true;
+    for (int j = 0; j < n; ++j) {
+        pipe = pipe && tn_pipe_ok(M, jobs[j].ldy, jobs[j].ldx, jobs[j].N, jobs[j].K);
+        tiles += cdiv(jobs[j].N, BIG) * cdiv(jobs[j].K, BIG);
     }
-    p.outf = partial; p.ldf = K; p.split_stride = (int64_t)N * K;
-    hipError_t e = t.big ? run_tn_big<EPI_F32_STORE>(p, s) : run<128, 128, 2, 2, true, true, EPI_F32_STORE>(p, s);
-    if (e != hipSuccess) return e;
-    const int64_t n4 = (int64_t)N * K / 4;
-    const int blocks = (int)std::min<int64_t>(cdiv(n4, 256), 4096);
-    PROF_LAUNCH(KC_SPLITK_REDUCE, 4.0 * n4 * 4 * (t.splits + 2), s,
-                hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, (const float4*)partial,
-                                   (float4*)dW, n4, t.splits, n4));
-    return hipGetLastError();
+    if (pipe && tiles >= 8) return run_tn_group(jobs, n, M, partial, partial_elems, s);
+    // small or unaligned products: the generic 128x128 kernel, one job at a time
+    for (int j = 0; j < n; ++j) {
+        const TnJobDesc& d = jobs[j];
+        GemmParams p{};
+        p.A = d.dY; p.B = d.X; p.lda = d.ldy; p.ldb = d.ldx; p.M = d.N; p.N = d.K; p.nk_total = M / BK;
+        p.splits = 1; p.dbias = d.db; p.outf = d.dW; p.ldf = d.K;
+        hipError_t e = run<128, 128, 2, 2, true, true, EPI_F32_ACC>(p, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+int64_t gemm_tn_group_partial_elems(const TnJobDesc* jobs, int n, int M) {
+    int64_t tiles = 0, elems = 0;
+    for (int j = 0; j < n; ++j) {
+        tiles += cdiv(jobs[j].N, BIG) * cdiv(jobs[j].K, BIG);
+        elems += (int64_t)jobs[j].N * jobs[j].K;
+    }
+    const int sp = tn_group_splits(tiles, M / BK);
+    return sp > 1 ? sp * elems : 0;
 }

@@ -2,8 +2,8 @@
 // before attention and before the feed-forward part; §4 precision paragraph:
 // statistics in fp32).  One wavefront per row: each lane keeps C/64 values in
 // registers, so a row is read once; statistics are wavefront reductions.
-// The backward also adds the row's input gradient into the residual-stream
-// gradient and produces per-block fp32 partial column sums of dy*xhat and dy,
+// The backward also adds the row's input gradient to the residual-stream
+// gradient (read from one buffer, written to another or the same one) and produces per-block fp32 partial column sums of dy*xhat and dy,
 // which a second small kernel folds into dw, db.
 #include "common.h"
 #include "kernels.h"
@@ -83,8 +83,9 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const uint16_t* __restrict_
 template <int VEC, int NV>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy,
                                                      const float* __restrict__ w, const float* __restrict__ mean,
-                                                     const float* __restrict__ rstd, uint16_t* __restrict__ dres,
-                                                     int accumulate, float* __restrict__ partial, int64_t rows) {
+                                                     const float* __restrict__ rstd, const uint16_t* dres_in,
+                                                     uint16_t* dres, int accumulate, float* __restrict__ partial,
+                                                     int64_t rows) {
     constexpr int C = NV * 64 * VEC;
     typedef typename Vec<VEC>::T VT;
     __shared__ float red[ROWS_PER_BLOCK][2][C];
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const uint16_t* __restrict_
     auto load = [&](int64_t row, RowIn& in) {
         const VT* xr = (const VT*)(x + row * C);
         const VT* dyr = (const VT*)(dy + row * C);
-        const VT* dr = (const VT*)(dres + row * C);
+        const VT* dr = (const VT*)(dres_in + row * C);
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             in.xv[j] = xr[j * 64 + lane];
@@ -215,11 +216,12 @@ hipError_t ln_fwd_t(const uint16_t* x, const float* w, const float* b, uint16_t*
 
 template <int VEC, int NV>
 hipError_t ln_bwd_t(const uint16_t* x, const uint16_t* dy, const float* w, const float* mean, const float* rstd,
-                    uint16_t* dres, int accumulate, float* dw, float* db, float* partial, int64_t rows,
+                    const uint16_t* dres_in, uint16_t* dres, int accumulate, float* dw, float* db, float* partial,
+                    int64_t rows,
                     hipStream_t s) {
     constexpr int C = NV * 64 * VEC;
     int blocks = ln_blocks(rows);
-    PROF_LAUNCH(KC_LN_BWD, 2.0 * rows * C * (accumulate ? 4 : 3), s, hipLaunchKernelGGL((ln_bwd_kernel<VEC, NV>), dim3(blocks), dim3(256), 0, s, x, dy, w, mean, rstd, dres,
+    PROF_LAUNCH(KC_LN_BWD, 2.0 * rows * C * (accumulate ? 4 : 3), s, hipLaunchKernelGGL((ln_bwd_kernel<VEC, NV>), dim3(blocks), dim3(256), 0, s, x, dy, w, mean, rstd, dres_in, dres,
                        accumulate, partial, rows));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -257,12 +259,13 @@ hipError_t launch_layernorm_fwd(const uint16_t* x, const float* w, const float* 
 int64_t layernorm_bwd_partial_elems(int64_t rows, int C) { return (int64_t)ln_blocks(rows) * 2 * C; }
 
 hipError_t launch_layernorm_bwd(const uint16_t* x, const uint16_t* dy, const float* w, const float* mean,
-                                const float* rstd, uint16_t* dres, int accumulate, float* dw, float* db,
+                                const float* rstd, const uint16_t* dres_in, uint16_t* dres, int accumulate,
+                                float* dw, float* db,
                                 float* partial, int64_t rows, int C, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
     switch (C) {
 #define X(c, vec, nv) \
-    case c: return ln_bwd_t<vec, nv>(x, dy, w, mean, rstd, dres, accumulate, dw, db, partial, rows, s);
+    case c: return ln_bwd_t<vec, nv>(x, dy, w, mean, rstd, dres_in, dres, accumulate, dw, db, partial, rows, s);
         LN_CASES(X)
 #undef X
     }

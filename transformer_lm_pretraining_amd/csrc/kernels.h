@@ -21,6 +21,21 @@ hipError_t launch_gemm_nt_dgelu(const uint16_t* A, int64_t lda, const uint16_t* 
 // M % 64 == 0, N % 8 == 0, K % 8 == 0.
 hipError_t launch_gemm_tn_acc(const uint16_t* dY, int64_t ldy, const uint16_t* X, int64_t ldx, int M, int N, int K,
                               float* dW, float* dbias, float* partial, int64_t partial_elems, hipStream_t s);
+// One weight-gradient product dW[N][K] (+)= dY^T X over M tokens (dY [M][N] row
+// stride ldy, X [M][K] row stride ldx), db[N] (+)= column sums of dY (may be null).
+struct TnJobDesc {
+    const uint16_t* dY;
+    int64_t ldy;
+    const uint16_t* X;
+    int64_t ldx;
+    int N, K;
+    float* dW;
+    float* db;
+};
+// Up to 4 products over the same M tokens in one launch (+ one reduce when split).
+hipError_t launch_gemm_tn_group(const TnJobDesc* jobs, int n, int M, float* partial, int64_t partial_elems,
+                                hipStream_t s);
+int64_t gemm_tn_group_partial_elems(const TnJobDesc* jobs, int n, int M);
 int64_t gemm_tn_partial_elems(int M, int N, int K);
 
 // ---- LayerNorm / elementwise / loss (k_norm.hip, k_misc.hip) ----------------
@@ -28,9 +43,10 @@ bool layernorm_supports(int C);
 hipError_t launch_layernorm_fwd(const uint16_t* x, const float* w, const float* b, uint16_t* y, float* mean,
                                 float* rstd, int64_t rows, int C, hipStream_t s);
 int64_t layernorm_bwd_partial_elems(int64_t rows, int C);
+// dres = (accumulate ? dres_in : 0) + dx; dres_in may equal dres (in place)
 hipError_t launch_layernorm_bwd(const uint16_t* x, const uint16_t* dy, const float* w, const float* mean,
-                                const float* rstd, uint16_t* dres, int accumulate, float* dw, float* db,
-                                float* partial, int64_t rows, int C, hipStream_t s);
+                                const float* rstd, const uint16_t* dres_in, uint16_t* dres, int accumulate,
+                                float* dw, float* db, float* partial, int64_t rows, int C, hipStream_t s);
 int64_t colsum_partial_elems(int64_t rows, int N);
 hipError_t launch_bias_gelu_fwd(const uint16_t* u, const float* b, uint16_t* pre, uint16_t* g, int64_t rows, int N,
                                 hipStream_t s);
