@@ -86,26 +86,22 @@ __device__ __forceinline__ void transpose8x8(const u32x4* in, u32x4* out) {
     }
 }
 
-// tanh(a) = 1 - 2 / (exp(2a) + 1), with the hardware base-2 exponential; |a| is
-// clamped at 15 where tanh is 1 to fp32 precision (keeps exp finite).
-__device__ __forceinline__ float fast_tanh(float a) {
-    a = fminf(fmaxf(a, -15.0f), 15.0f);
-    const float e = __builtin_amdgcn_exp2f(a * 2.8853900817779268f);  // exp(2a) = 2^(2a log2 e)
-    return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+// GPT-2's tanh-form GELU and its derivative, evaluated in fp32.  With
+// a = sqrt(2/pi) (x + 0.044715 x^3), 0.5 (1 + tanh(a)) is the logistic sigmoid
+// s = 1 / (1 + exp(-2a)), so GELU(x) = x s and GELU'(x) = s + x s (1 - s) da2/dx
+// with da2/dx = 2 sqrt(2/pi) (1 + 3 * 0.044715 x^2).  exp(-2a) is taken as the
+// hardware base-2 exponential of x (c0 + c1 x^2); where it overflows, s is 0.
+__device__ __forceinline__ float gelu_sigmoid(float x, float x2) {
+    const float c0 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+    const float c1 = c0 * 0.044715f;
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * fmaf(c1, x2, c0)));
 }
-
-// GPT-2's tanh-form GELU and its derivative, evaluated in fp32.
-__device__ __forceinline__ float gelu_f(float x) {
-    const float k = 0.7978845608028654f;  // sqrt(2/pi)
-    float a = k * (x + 0.044715f * x * x * x);
-    return 0.5f * x * (1.0f + fast_tanh(a));
-}
+__device__ __forceinline__ float gelu_f(float x) { return x * gelu_sigmoid(x, x * x); }
 __device__ __forceinline__ float gelu_grad_f(float x) {
-    const float k = 0.7978845608028654f;
-    float x2 = x * x;
-    float a = k * (x + 0.044715f * x2 * x);
-    float t = fast_tanh(a);
-    return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * k * (1.0f + 3.0f * 0.044715f * x2);
+    const float x2 = x * x;
+    const float s = gelu_sigmoid(x, x2);
+    const float d = fmaf(2.0f * 0.7978845608028654f * 3.0f * 0.044715f, x2, 2.0f * 0.7978845608028654f);
+    return fmaf(x * s * (1.0f - s), d, s);
 }
 
 __host__ __device__ static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

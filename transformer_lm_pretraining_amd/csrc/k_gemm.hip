@@ -879,6 +879,25 @@ bool tn_pipe_ok(int M, int64_t ldy, int64_t ldx, int N, int K) {
            (int64_t)M * ldx < (1ll << 31);
 }
 
+// A single product with more tiles than CUs whose last pass would run mostly
+// idle: the output rows that fill whole passes run unsplit and the remaining
+// rows run as a second product split over tokens, so the last pass is short
+// instead of mostly empty.  Returns the split row and the tail's split count.
+bool tn_tail_plan(int N, int K, int nk, int* full_rows, int* tail_splits) {
+    const int64_t tm = cdiv(N, BIG), tn = cdiv(K, BIG), tiles = tm * tn;
+    if (tiles < NUM_CU || (tiles % NUM_CU) * 5 >= NUM_CU * 4 || tiles % NUM_CU == 0) return false;
+    const int64_t full_m = (tiles / NUM_CU) * NUM_CU / tn;
+    if (full_m <= 0 || full_m >= tm) return false;
+    const int sp = tn_group_splits((tm - full_m) * tn, nk);
+    if (sp < 2) return false;
+    const double passes_split = std::ceil((double)(full_m * tn) / NUM_CU) +
+                                std::ceil((double)((tm - full_m) * tn * sp) / NUM_CU) / sp;
+    if (passes_split >= std::ceil((double)tiles / NUM_CU) - 0.25) return false;
+    *full_rows = (int)(full_m * BIG);
+    *tail_splits = sp;
+    return true;
+}
+
 // Runs jobs [0, n) of equal token count M as one grouped 256x256-tile launch
 // (plus one reduce launch when split).
 hipError_t run_tn_group(const TnJobDesc* jobs, int n, int M, float* partial, int64_t partial_elems, hipStream_t s) {
@@ -981,6 +1000,15 @@ hipError_t launch_gemm_tn_group(const TnJobDesc* jobs, int n, int M, float* part
         pipe = pipe && tn_pipe_ok(M, jobs[j].ldy, jobs[j].ldx, jobs[j].N, jobs[j].K);
         tiles += cdiv(jobs[j].N, BIG) * cdiv(jobs[j].K, BIG);
     }
+    int full_rows = 0, tail_sp = 1;
+    if (pipe && n == 1 && tn_tail_plan(jobs[0].N, jobs[0].K, M / BK, &full_rows, &tail_sp)) {
+        const TnJobDesc& d = jobs[0];
+        const TnJobDesc head{d.dY, d.ldy, d.X, d.ldx, full_rows, d.K, d.dW, d.db};
+        const TnJobDesc tail{d.dY + full_rows, d.ldy, d.X, d.ldx, d.N - full_rows, d.K,
+                             d.dW + (int64_t)full_rows * d.K, d.db ? d.db + full_rows : nullptr};
+        hipError_t e = run_tn_group(&head, 1, M, nullptr, 0, s);
+        return e != hipSuccess ? e : run_tn_group(&tail, 1, M, partial, partial_elems, s);
+    }
     if (pipe && tiles >= 8) return run_tn_group(jobs, n, M, partial, partial_elems, s);
     // small or unaligned products: the generic 128x128 kernel, one job at a time
     for (int j = 0; j < n; ++j) {
@@ -995,6 +1023,9 @@ hipError_t launch_gemm_tn_group(const TnJobDesc* jobs, int n, int M, float* part
 }
 
 int64_t gemm_tn_group_partial_elems(const TnJobDesc* jobs, int n, int M) {
+    int full_rows = 0, tail_sp = 1;
+    if (n == 1 && tn_tail_plan(jobs[0].N, jobs[0].K, M / BK, &full_rows, &tail_sp))
+        return (int64_t)tail_sp * (jobs[0].N - full_rows) * jobs[0].K;
     int64_t tiles = 0, elems = 0;
     for (int j = 0; j < n; ++j) {
         tiles += cdiv(jobs[j].N, BIG) * cdiv(jobs[j].K, BIG);
