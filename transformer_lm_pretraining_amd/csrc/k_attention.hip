@@ -35,6 +35,16 @@ constexpr float LN2 = 0.6931471805599453f;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
+// Row block of a workgroup, 0 = the heaviest.  Workgroups reach the eight XCDs
+// round-robin by linear index; with a 1-D grid whose index runs over the B*H
+// heads fastest and the row blocks in order of decreasing causal work, every
+// XCD receives an equal share of each work level (a 2-D grid with the row
+// block fastest would send all of one row block to one XCD).
+__device__ __forceinline__ int attn_unit(int BH, int& bh) {
+    bh = (int)(blockIdx.x % (unsigned)BH);
+    return (int)(blockIdx.x / (unsigned)BH);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // A operand X^T (rows = features col0..col0+31, k = 16 streamed rows of step ks) from a
@@ -87,13 +97,15 @@ struct Stage {
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __restrict__ qkv,
                                                           uint16_t* __restrict__ out, float* __restrict__ lse,
-                                                          int T, int H, int C, float sl) {
+                                                          int T, int H, int C, int BH, float sl) {
     constexpr int LD = D + 8;
     constexpr int KK = D / 16, DT = D / 32;
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][KVB * LD];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][KVB * LD];
-    const int bh = blockIdx.y, b = bh / H, h = bh % H;
-    const int q0 = (gridDim.x - 1 - blockIdx.x) * QB;  // heaviest blocks first
+    int bh;
+    const int nqb = (int)(gridDim.x / (unsigned)BH);
+    const int q0 = (nqb - 1 - attn_unit(BH, bh)) * QB;  // heaviest blocks first
+    const int b = bh / H, h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
     const int64_t ld = 3 * (int64_t)C;
     const uint16_t* Qg = qkv + (int64_t)b * T * ld + h * D;
@@ -255,15 +267,16 @@ __global__ __launch_bounds__(256, 2) void attn_dkdv_kernel(const uint16_t* __res
                                                            const float* __restrict__ lse,
                                                            const float* __restrict__ dvec,
                                                            uint16_t* __restrict__ dqkv, int T, int H, int C,
-                                                           float sl, float scale) {
+                                                           int BH, float sl, float scale) {
     constexpr int LD = D + 8;
     constexpr int KK = D / 16, DT = D / 32;
     __shared__ __attribute__((aligned(16))) uint16_t sQ[2][KVB * LD];
     __shared__ __attribute__((aligned(16))) uint16_t sdO[2][KVB * LD];
     __shared__ __attribute__((aligned(16))) float sL[2][KVB];
     __shared__ __attribute__((aligned(16))) float sDv[2][KVB];
-    const int bh = blockIdx.y, b = bh / H, h = bh % H;
-    const int k0 = blockIdx.x * QB;
+    int bh;
+    const int k0 = attn_unit(BH, bh) * QB;  // the first key blocks see the most queries
+    const int b = bh / H, h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
     const int64_t ld = 3 * (int64_t)C;
     const uint16_t* Qg = qkv + (int64_t)b * T * ld + h * D;
@@ -419,13 +432,15 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const uint16_t* __restr
                                                          const float* __restrict__ lse,
                                                          const float* __restrict__ dvec,
                                                          uint16_t* __restrict__ dqkv, int T, int H, int C,
-                                                         float sl, float scale) {
+                                                         int BH, float sl, float scale) {
     constexpr int LD = D + 8;
     constexpr int KK = D / 16, DT = D / 32;
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][KVB * LD];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][KVB * LD];
-    const int bh = blockIdx.y, b = bh / H, h = bh % H;
-    const int q0 = (gridDim.x - 1 - blockIdx.x) * QB;
+    int bh;
+    const int nqb = (int)(gridDim.x / (unsigned)BH);
+    const int q0 = (nqb - 1 - attn_unit(BH, bh)) * QB;
+    const int b = bh / H, h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
     const int64_t ld = 3 * (int64_t)C;
     const uint16_t* Qg = qkv + (int64_t)b * T * ld + h * D;
@@ -543,9 +558,9 @@ double attn_work(int B, int T, int H, int D, int matmuls) {
 template <int D>
 hipError_t fwd_t(const uint16_t* qkv, uint16_t* out, float* lse, int B, int T, int H, int C, hipStream_t s) {
     const float sl = LOG2E / sqrtf((float)D);
-    dim3 grid((unsigned)cdiv(T, QB), (unsigned)(B * H));
+    dim3 grid((unsigned)(cdiv(T, QB) * B * H));
     PROF_LAUNCH(KC_ATTN_FWD, attn_work(B, T, H, D, 2), s,
-                hipLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(256), 0, s, qkv, out, lse, T, H, C, sl));
+                hipLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(256), 0, s, qkv, out, lse, T, H, C, B * H, sl));
     return hipGetLastError();
 }
 
@@ -560,15 +575,15 @@ hipError_t bwd_t(const uint16_t* qkv, const uint16_t* out, const uint16_t* dout,
                                    dim3(256), 0, s, out, dout, dvec, B, T, H, C));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid((unsigned)cdiv(T, QB), (unsigned)(B * H));
+    dim3 grid((unsigned)(cdiv(T, QB) * B * H));
     PROF_LAUNCH(KC_ATTN_DKDV, attn_work(B, T, H, D, 4), s,
                 hipLaunchKernelGGL(attn_dkdv_kernel<D>, grid, dim3(256), 0, s, qkv, dout, lse, dvec, dqkv, T, H, C,
-                                   scale_log2, scale));
+                                   B * H, scale_log2, scale));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     PROF_LAUNCH(KC_ATTN_DQ, attn_work(B, T, H, D, 3), s,
                 hipLaunchKernelGGL(attn_dq_kernel<D>, grid, dim3(256), 0, s, qkv, dout, lse, dvec, dqkv, T, H, C,
-                                   scale_log2, scale));
+                                   B * H, scale_log2, scale));
     return hipGetLastError();
 }
 
