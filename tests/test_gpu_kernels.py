@@ -253,6 +253,29 @@ def test_attention_parity(gpu_lib, B, T, H, C):
         assert cosine(got, _merge(ref)) >= 0.999, part
 
 
+@pytest.mark.parametrize("slope", [0.1, -0.1])
+def test_attention_drifting_scores(gpu_lib, slope):
+    """Scores that rise (or fall) by ~6 nats per 64-key block: the forward's
+    running reference max has to move on later blocks, not only the first."""
+    import torch
+    from transformer_lm_pretraining_amd import lib
+    B, T, H, C = 1, 512, 2, 128
+    d = C // H
+    say("attention drifting", slope)
+    qkv = synth.normal((B * T, 3 * C), std=0.3, seed=83)
+    pos = np.arange(T, dtype=np.float64)[:, None]
+    for h in range(H):
+        qkv[:, h * d:(h + 1) * d] += 1.0                                # q ~ all-ones direction
+        qkv[:, C + h * d:C + (h + 1) * d] += slope * 8.0 * pos / d      # q.k/sqrt(d) ~ slope * key index
+    qkv = bf16_round(qkv)
+    out, lse = lib.attention_fwd(to_dev_bf16(qkv), B, T, H, C)
+    torch.cuda.synchronize()
+    q, k, v = _split(qkv, B, T, H, C)
+    o, p, lse_r = ops.attention_fwd(q, k, v)
+    assert rel_l2(host(out), _merge(o)) <= 1e-2
+    np.testing.assert_allclose(host(lse), lse_r, atol=2e-3 * max(1.0, np.abs(lse_r).max() / 8))
+
+
 def test_attention_full_size_sampled_heads(gpu_lib):
     import torch
     from transformer_lm_pretraining_amd import lib

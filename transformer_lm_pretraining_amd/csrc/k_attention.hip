@@ -32,6 +32,7 @@ constexpr int QB = 128;     // rows owned per workgroup (4 waves x 32)
 constexpr int KVB = 64;     // streamed rows per step
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+constexpr float RESCALE_LOG2 = 8.0f;  // forward: largest probability 2^8 before a rescale
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
@@ -92,8 +93,9 @@ struct Stage {
 // issued, the 8 V^T fragments for this block read (their latency hidden by the
 // softmax), then the 8 O^T MFMAs.  Scores stay in raw units: the max is taken
 // on raw scores and exp2(s * scale*log2e - m * scale*log2e) is one FMA + exp.
-// Masks are applied only on blocks that straddle the diagonal, and the output
-// accumulators are rescaled only when some query's running max moved.
+// Masks are applied only on blocks that straddle the diagonal; the reference
+// max (and with it O and l) is moved only when a block max exceeds it by more
+// than a factor 2^RESCALE_LOG2 in probability.
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __restrict__ qkv,
                                                           uint16_t* __restrict__ out, float* __restrict__ lse,
@@ -176,36 +178,41 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[st][r]);
             mloc = fmaxf(mloc, __shfl_xor(mloc, 32, WAVE));
-            const float m_new = fmaxf(m_run, mloc);  // finite: key 0 is visible to every query
-            const float mb = m_new * sl;
-            const float alpha = fast_exp2(m_run * sl - mb);
-            float lsum = 0.f;
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float pr = fast_exp2(fmaf(sacc[st][r], sl, -mb));
-                    sacc[st][r] = pr;
-                    lsum += pr;
-                }
-            l_run = l_run * alpha + lsum;
-            m_run = m_new;
-            if (__any(alpha != 1.0f)) {
+            // The reference m_run moves only when some query's block max exceeds it
+            // by more than RESCALE_LOG2 (log2 units), so probabilities stay below
+            // 2^RESCALE_LOG2 and the O / l rescale is rare; numerator and denominator
+            // share the reference, so the result is unchanged.  The first block
+            // always sets it (m_run = -inf; key 0 is visible to every query).
+            if (__any((mloc - m_run) * sl > RESCALE_LOG2)) {
+                const float m_new = fmaxf(m_run, mloc);
+                const float alpha = fast_exp2((m_run - m_new) * sl);
+                l_run *= alpha;
+                m_run = m_new;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
             }
+            const float mb = m_run * sl;
+            bf16x8 pf[KVB / 16];
+            float ls[KVB / 16];
 #pragma unroll
             for (int ks = 0; ks < KVB / 16; ++ks) {
                 const int st = ks >> 1, half = ks & 1;
                 float pv[8];
+                ls[ks] = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pv[e] = sacc[st][8 * half + e];
-                const bf16x8 pf = pack8(pv);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(vfr[ks][dt], pf, acc[dt]);
+                for (int e = 0; e < 8; ++e) {
+                    pv[e] = fast_exp2(fmaf(sacc[st][8 * half + e], sl, -mb));
+                    ls[ks] += pv[e];
+                }
+                pf[ks] = pack8(pv);
             }
+            l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+#pragma unroll
+            for (int ks = 0; ks < KVB / 16; ++ks)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(vfr[ks][dt], pf[ks], acc[dt]);
         }
         if (kb + 1 < nkv) {
             // buffer buf^1 was last read in step kb-1, before the previous barrier
