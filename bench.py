@@ -33,9 +33,9 @@ METRIC = "GPT-2 124M train tokens/s on 1 MI355X (19x1024x9 accum); MFU vs bf16 p
 # kernel sources the counters were taken on: a changed source reports null.
 TRAFFIC_COUNTERS = {
     ("gpt2_124m", "gemm_nt"): {
-        "sources": {"k_gemm.hip": "cb1bf18581aa82aacf192ed9e8c281ad36763494a39854c7c5218c087c1fcb9a",
-                    "common.h": "09cdf91791baa2de19911f14e9fb85ba680bbb96ba8302f6d0ef6c9caca3aaf4"},
-        "fetch_kib": 116826.06, "fetch_scale": 1.99994, "write_kib": 69599.57, "write_scale": 1.0,
+        "sources": {"k_gemm.hip": "5291aaf58da4036a8a92fd0d083edc88ab3ce325a66942385a1e3e596891816f",
+                    "common.h": "90b08ce8f63df1b9fe6c37a5739d4d05fc5bb78251ac31697c268a39bee6243c"},
+        "fetch_kib": 115239.13, "fetch_scale": 1.99994, "write_kib": 64086.49, "write_scale": 1.0,
     },
 }
 
