@@ -215,12 +215,15 @@ def test_zero_embedding_loss_is_ln_V_gpu(gpu_lib):
     assert np.all(wte_g[cfg.V:] == 0)
 
 
-def test_gpt2_shapes_two_layers_parity(gpu_lib):
-    """The 124M layer shapes (C=768, 12 heads of 64, T=1024, Vp=50,304) at 2 layers, B=2."""
+@pytest.mark.parametrize("L,B", [(2, 2), (3, 1)])
+def test_gpt2_shapes_two_layers_parity(gpu_lib, L, B):
+    """The 124M layer shapes (C=768, 12 heads of 64, T=1024, Vp=50,304) at 2 layers, B=2,
+    and at 3 layers, B=1 (the weight gradients of two blocks go out in one launch; with
+    an odd layer count the first block's go alone)."""
     import torch
-    cfg = Config(L=2, H=12, C=768, V=50257, Vp=50304, Tmax=1024)
-    B, T = 2, 1024
-    say("gpt2-shape 2 layers")
+    cfg = Config(L=L, H=12, C=768, V=50257, Vp=50304, Tmax=1024)
+    T = 1024
+    say("gpt2-shape layers", L, "batch", B)
     P = init_params(cfg, 1337)
     tok, tgt = synth.micro_batches(1, B, T, cfg.V, seed=21)[0]
     model = make_model(cfg, B, T, init=oracle.flatten(cfg, P))

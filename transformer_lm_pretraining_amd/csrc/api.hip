@@ -90,7 +90,7 @@ struct LayerActs {
 struct ActsPlan {
     std::vector<LayerActs> layer;
     int64_t xfinal, lnf, meanf, rstdf, logits, loss_rows;
-    int64_t d_res[3], d_ln, d_big, d_qkv, d_att;
+    int64_t d_res[5], d_ln, d_big[2], d_qkv[2], d_att;
     int64_t total;
 };
 struct ScratchPlan {
@@ -132,13 +132,24 @@ ActsPlan plan_acts(const gpt2_config& c) {
     a.rstdf = take(BT * 4);
     a.logits = take(BT * (int64_t)c.Vp * 2);
     a.loss_rows = take(BT * 4);
-    for (int i = 0; i < 3; ++i) a.d_res[i] = take(BT * C * 2);
+    for (int i = 0; i < 5; ++i) a.d_res[i] = take(BT * C * 2);
     a.d_ln = take(BT * C * 2);
-    a.d_big = take(BT * 4 * C * 2);
-    a.d_qkv = take(BT * 3 * C * 2);
+    for (int i = 0; i < 2; ++i) {
+        a.d_big[i] = take(BT * 4 * C * 2);
+        a.d_qkv[i] = take(BT * 3 * C * 2);
+    }
     a.d_att = take(BT * C * 2);
     a.total = off;
     return a;
+}
+
+// The four weight-gradient products of one block, shapes only.
+void block_dw_shapes(const gpt2_config& c, TnJobDesc* jobs) {
+    const int C = c.C;
+    jobs[0] = {nullptr, C, nullptr, 4 * C, C, 4 * C, nullptr, nullptr};
+    jobs[1] = {nullptr, 4 * C, nullptr, C, 4 * C, C, nullptr, nullptr};
+    jobs[2] = {nullptr, C, nullptr, C, C, C, nullptr, nullptr};
+    jobs[3] = {nullptr, 3 * C, nullptr, C, 3 * C, C, nullptr, nullptr};
 }
 
 ScratchPlan plan_scratch(const gpt2_config& c) {
@@ -157,10 +168,8 @@ ScratchPlan plan_scratch(const gpt2_config& c) {
     off = align_up(off + s.col_partial_elems * 4);
     {
         // one block's grouped weight-gradient products, and the lm_head's
-        const TnJobDesc blk[4] = {{nullptr, C, nullptr, 4 * C, (int)C, 4 * (int)C, nullptr, nullptr},
-                                  {nullptr, 4 * C, nullptr, C, 4 * (int)C, (int)C, nullptr, nullptr},
-                                  {nullptr, C, nullptr, C, (int)C, (int)C, nullptr, nullptr},
-                                  {nullptr, 3 * C, nullptr, C, 3 * (int)C, (int)C, nullptr, nullptr}};
+        TnJobDesc blk[4];
+        block_dw_shapes(c, blk);
         s.splitk_elems = std::max(gemm_tn_group_partial_elems(blk, 4, (int)BT),
                                   gemm_tn_partial_elems((int)BT, c.Vp, (int)C));
     }
@@ -314,7 +323,8 @@ int run_forward(gpt2_handle* h, const int32_t* tok, const int32_t* tgt, float dl
 // The four weight-gradient products of block l, one grouped launch (run once
 // the block's input gradient is done, so their dY tensors are all still held:
 // the residual-stream gradients at the block output and at x_mid, dpre, dqkv).
-TnJobDesc block_dw_job(gpt2_handle* h, int l, int which, const uint16_t* d_out, const uint16_t* d_mid) {
+TnJobDesc block_dw_job(gpt2_handle* h, int l, int which, const uint16_t* d_out, const uint16_t* d_mid,
+                       const uint16_t* d_pre, const uint16_t* d_qkv) {
     const gpt2_config& c = h->cfg;
     const int C = c.C;
     const LayerActs& la = h->acts.layer[l];
@@ -322,14 +332,25 @@ TnJobDesc block_dw_job(gpt2_handle* h, int l, int which, const uint16_t* d_out, 
         case 0:  // FC-proj: x_next = x_mid + gel . W_fp^T + b_fp
             return {d_out, C, h->act<uint16_t>(la.gel), 4 * C, C, 4 * C, h->G(h->i_mat(l, 3)), h->G(h->i_vec(l, 7))};
         case 1:  // FC: pre = ln2 . W_fc^T + b_fc
-            return {h->act<uint16_t>(h->acts.d_big), 4 * C, h->act<uint16_t>(la.ln2), C, 4 * C, C, h->G(h->i_mat(l, 2)),
-                    h->G(h->i_vec(l, 6))};
+            return {d_pre, 4 * C, h->act<uint16_t>(la.ln2), C, 4 * C, C, h->G(h->i_mat(l, 2)), h->G(h->i_vec(l, 6))};
         case 2:  // attention projection: x_mid = x + att . W_p^T + b_p
             return {d_mid, C, h->act<uint16_t>(la.att), C, C, C, h->G(h->i_mat(l, 1)), h->G(h->i_vec(l, 3))};
         default:  // QKV: qkv = ln1 . W_qkv^T + b_qkv
-            return {h->act<uint16_t>(h->acts.d_qkv), 3 * C, h->act<uint16_t>(la.ln1), C, 3 * C, C,
-                    h->G(h->i_mat(l, 0)), h->G(h->i_vec(l, 2))};
+            return {d_qkv, 3 * C, h->act<uint16_t>(la.ln1), C, 3 * C, C, h->G(h->i_mat(l, 0)), h->G(h->i_vec(l, 2))};
     }
+}
+
+// Whether the backward launches the weight gradients of two consecutive blocks
+// together: when one block's products are too few tiles to fill the CUs (they
+// would be split over tokens, with fp32 partials and a reduce) and two blocks'
+// products fill them without a split.
+bool pair_block_dw(const gpt2_config& c) {
+    if (c.L < 2) return false;
+    TnJobDesc j[8];
+    block_dw_shapes(c, j);
+    block_dw_shapes(c, j + 4);
+    const int BT = c.B * c.T;
+    return gemm_tn_group_partial_elems(j, 4, BT) > 0 && gemm_tn_group_partial_elems(j, 8, BT) == 0;
 }
 
 int run_backward(gpt2_handle* h, hipStream_t s) {
@@ -339,12 +360,18 @@ int run_backward(gpt2_handle* h, hipStream_t s) {
     float* colp = (float*)(h->S() + h->scr.col_partial);
     float* splitk = (float*)(h->S() + h->scr.splitk);
     const int64_t splitk_n = h->scr.splitk_elems;
-    // residual-stream gradients rotate through three buffers: a block reads the one
-    // at its output, writes the one at x_mid and the one at its input
-    uint16_t* d_res[3] = {h->act<uint16_t>(A.d_res[0]), h->act<uint16_t>(A.d_res[1]), h->act<uint16_t>(A.d_res[2])};
+    // Residual-stream gradients rotate through NR buffers: a block reads the one at
+    // its output and writes the ones at x_mid and at its input.  When the weight
+    // gradients of two blocks are launched together, the first block's output and
+    // x_mid gradients, dpre and dqkv must outlive the second block's backward: five
+    // residual buffers and a second dpre / dqkv then keep them.
+    const bool pair = pair_block_dw(c);
+    const int NR = pair ? 5 : 3;
+    uint16_t* d_res[5];
+    for (int i = 0; i < 5; ++i) d_res[i] = h->act<uint16_t>(A.d_res[i]);
     uint16_t* d_ln = h->act<uint16_t>(A.d_ln);
-    uint16_t* d_big = h->act<uint16_t>(A.d_big);
-    uint16_t* d_qkv = h->act<uint16_t>(A.d_qkv);
+    uint16_t* d_big_buf[2] = {h->act<uint16_t>(A.d_big[0]), h->act<uint16_t>(A.d_big[1])};
+    uint16_t* d_qkv_buf[2] = {h->act<uint16_t>(A.d_qkv[0]), h->act<uint16_t>(A.d_qkv[1])};
     uint16_t* d_att = h->act<uint16_t>(A.d_att);
     uint16_t* dlogits = h->act<uint16_t>(A.logits);
 
@@ -356,11 +383,15 @@ int run_backward(gpt2_handle* h, hipStream_t s) {
     HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(A.xfinal), d_ln, h->P(h->i_lnf(0)), h->act<float>(A.meanf),
                                 h->act<float>(A.rstdf), d_res[ri], d_res[ri], 0, h->G(h->i_lnf(0)),
                                 h->G(h->i_lnf(1)), colp, BT, C, s));
+    TnJobDesc jobs[8];
+    int pending = 0;  // products of a block waiting for its pair
     for (int l = c.L - 1; l >= 0; --l) {
         const LayerActs& la = A.layer[l];
-        uint16_t* d_out = d_res[ri];            // gradient at the block output
-        uint16_t* d_mid = d_res[(ri + 1) % 3];  // at x_mid
-        uint16_t* d_in = d_res[(ri + 2) % 3];   // at the block input
+        uint16_t* d_out = d_res[ri];             // gradient at the block output
+        uint16_t* d_mid = d_res[(ri + 1) % NR];  // at x_mid
+        uint16_t* d_in = d_res[(ri + 2) % NR];   // at the block input
+        uint16_t* d_big = d_big_buf[pending ? 1 : 0];
+        uint16_t* d_qkv = d_qkv_buf[pending ? 1 : 0];
         // FC-proj input gradient, taken through GELU in the epilogue: d_big = dpre
         HIPCHK(launch_gemm_nt_dgelu(d_out, C, h->WT(h->i_mat(l, 3)), C, BT, 4 * C, C, h->act<uint16_t>(la.pre), d_big,
                                     4 * C, s));
@@ -381,12 +412,16 @@ int run_backward(gpt2_handle* h, hipStream_t s) {
         HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(la.x), d_ln, h->P(h->i_vec(l, 0)), h->act<float>(la.mean1),
                                     h->act<float>(la.rstd1), d_mid, d_in, 1, h->G(h->i_vec(l, 0)),
                                     h->G(h->i_vec(l, 1)), colp, BT, C, s));
-        // the block's weight and bias gradients
-        TnJobDesc jobs[4];
-        for (int k = 0; k < 4; ++k) jobs[k] = block_dw_job(h, l, k, d_out, d_mid);
-        HIPCHK(launch_gemm_tn_group(jobs, 4, BT, splitk, splitk_n, s));
-        ri = (ri + 2) % 3;
+        // the block's weight and bias gradients (with the previous block's when paired)
+        for (int k = 0; k < 4; ++k) jobs[pending + k] = block_dw_job(h, l, k, d_out, d_mid, d_big, d_qkv);
+        pending += 4;
+        if (!pair || pending == 8) {
+            HIPCHK(launch_gemm_tn_group(jobs, pending, BT, splitk, splitk_n, s));
+            pending = 0;
+        }
+        ri = (ri + 2) % NR;
     }
+    if (pending) HIPCHK(launch_gemm_tn_group(jobs, pending, BT, splitk, splitk_n, s));
     HIPCHK(launch_embedding_bwd(h->last_tok, d_res[ri], h->G(h->i_wte()), h->G(h->i_wpe()), c.B, c.T, C, c.V,
                                 (int32_t*)(h->S() + h->scr.emb_work), h->scr.emb_work_elems, s));
     return GPT2_OK;

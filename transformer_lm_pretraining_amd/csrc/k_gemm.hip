@@ -41,6 +41,7 @@ struct GemmParams {
     int nk_total;      // reduction length / BK
     int splits;
     int tiles_m, tiles_n;
+    int band;          // tile order: row tiles per band, 0 = round-robin bands of GROUP_M (see nt_tile)
     const float* bias;
     const uint16_t* res;   // residual (EPI_BF16 / EPI_BF16R) or pre-activation (EPI_DGELU)
     int64_t ldr;
@@ -52,6 +53,32 @@ struct GemmParams {
     int64_t split_stride;
     float* dbias;      // TN: bias gradient (column sums of A's source), may be null
 };
+
+// Output tile of work-group `lin` among tiles_m x tiles_n.  Work-groups reach
+// the 8 XCDs round-robin by linear index.  With band > 0 each XCD is given one
+// contiguous share of the tile sequence (the first ntiles % 8 XCDs one tile
+// more), and the sequence walks bands of `band` row tiles, row tile fastest:
+// with band = ceil(tiles_m / 8) each XCD keeps its own rows of A and streams
+// B about once (wide outputs such as the vocabulary projection).  With
+// band = 0 the sequence is dealt round-robin (split into 8 contiguous shares
+// when ntiles is a multiple of 8) over bands of GROUP_M row tiles; for outputs
+// a few tiles wide that keeps every column tile of a row tile on one XCD.
+__device__ __forceinline__ void nt_tile(int lin, int tiles_m, int tiles_n, int band, int& tm, int& tn) {
+    const int ntiles = tiles_m * tiles_n;
+    int pid;
+    if (band > 0) {
+        const int q = ntiles / NUM_XCD, r = ntiles % NUM_XCD, x = lin % NUM_XCD;
+        pid = x * q + min(x, r) + lin / NUM_XCD;
+    } else {
+        band = GROUP_M;
+        pid = (ntiles % NUM_XCD) == 0 ? (lin % NUM_XCD) * (ntiles / NUM_XCD) + lin / NUM_XCD : lin;
+    }
+    const int in_group = band * tiles_n;
+    const int first_m = (pid / in_group) * band;
+    const int gsize = min(tiles_m - first_m, band);
+    tm = first_m + (pid % in_group) % gsize;
+    tn = (pid % in_group) / gsize;
+}
 
 // Tile loader for an operand stored contiguous along the reduction:
 // element (row, k) at base[row * ld + k].
@@ -354,14 +381,9 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_w8_kernel(GemmParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
     const int wm = wave >> 2, wn = wave & 3;
 
-    const int ntiles = p.tiles_m * p.tiles_n;
-    int pid = blockIdx.x;
-    if ((ntiles % NUM_XCD) == 0) pid = (pid % NUM_XCD) * (ntiles / NUM_XCD) + pid / NUM_XCD;
-    const int in_group = GROUP_M * p.tiles_n;
-    const int first_m = (pid / in_group) * GROUP_M;
-    const int gsize = min(p.tiles_m - first_m, GROUP_M);
-    const int m0 = (first_m + (pid % in_group) % gsize) * BIG;
-    const int n0 = ((pid % in_group) / gsize) * BIG;
+    int tm, tn;
+    nt_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.band, tm, tn);
+    const int m0 = tm * BIG, n0 = tn * BIG;
     const int nk = p.nk_total * (BK / KD);
 
     // Lane q of load instruction i covers row (wave*IPO + i)*RPI + q/CPR at
@@ -585,7 +607,7 @@ __device__ __forceinline__ void lds_dma16_asm(const uint16_t* src, uint16_t* dst
 }
 
 // One weight-gradient product of a grouped launch.
-constexpr int TN_MAX_JOBS = 4;
+constexpr int TN_MAX_JOBS = 8;
 struct TnJob {
     const uint16_t* A;  // dY [tokens][M] (row stride lda)
     const uint16_t* B;  // X  [tokens][N] (row stride ldb)
@@ -839,6 +861,7 @@ hipError_t run_nt(GemmParams p, hipStream_t s) {
         (int64_t)p.M * p.lda < (1ll << 31) && (int64_t)p.N * p.ldb < (1ll << 31)) {
         p.tiles_m = (int)cdiv(p.M, BIG);
         p.tiles_n = (int)cdiv(p.N, BIG);
+        p.band = p.tiles_n >= 16 ? (int)std::max<int64_t>(1, cdiv(p.tiles_m, NUM_XCD)) : 0;
         const double work = 2.0 * p.M * p.N * (double)p.nk_total * BK;
         if (EPI == EPI_BF16 && p.res != nullptr)
             PROF_LAUNCH(gemm_class(false, EPI), work, s,

@@ -32,7 +32,7 @@ struct TnJobDesc {
     float* dW;
     float* db;
 };
-// Up to 4 products over the same M tokens in one launch (+ one reduce when split).
+// Up to 8 products over the same M tokens in one launch (+ one reduce when split).
 hipError_t launch_gemm_tn_group(const TnJobDesc* jobs, int n, int M, float* partial, int64_t partial_elems,
                                 hipStream_t s);
 int64_t gemm_tn_group_partial_elems(const TnJobDesc* jobs, int n, int M);
