@@ -90,7 +90,11 @@ struct LayerActs {
 struct ActsPlan {
     std::vector<LayerActs> layer;
     int64_t xfinal, lnf, meanf, rstdf, logits, loss_rows;
-    int64_t d_res[5], d_ln, d_big[2], d_qkv[2], d_att;
+    // backward temporaries; each block keeps the gradients its weight-gradient
+    // products read (output and x_mid residual gradients, dpre, dqkv) until the
+    // products of all blocks run together after the last block
+    std::vector<int64_t> d_out, d_mid, d_big, d_qkv;
+    int64_t d_in0, d_ln, d_att;
     int64_t total;
 };
 struct ScratchPlan {
@@ -132,16 +136,21 @@ ActsPlan plan_acts(const gpt2_config& c) {
     a.rstdf = take(BT * 4);
     a.logits = take(BT * (int64_t)c.Vp * 2);
     a.loss_rows = take(BT * 4);
-    for (int i = 0; i < 5; ++i) a.d_res[i] = take(BT * C * 2);
-    a.d_ln = take(BT * C * 2);
-    for (int i = 0; i < 2; ++i) {
-        a.d_big[i] = take(BT * 4 * C * 2);
-        a.d_qkv[i] = take(BT * 3 * C * 2);
+    for (int l = 0; l < c.L; ++l) {
+        a.d_out.push_back(take(BT * C * 2));
+        a.d_mid.push_back(take(BT * C * 2));
+        a.d_big.push_back(take(BT * 4 * C * 2));
+        a.d_qkv.push_back(take(BT * 3 * C * 2));
     }
+    a.d_in0 = take(BT * C * 2);
+    a.d_ln = take(BT * C * 2);
     a.d_att = take(BT * C * 2);
     a.total = off;
     return a;
 }
+
+// Blocks whose weight-gradient products go out in one grouped call.
+constexpr int DW_GROUP_BLOCKS = TN_GROUP_MAX / 4;
 
 // The four weight-gradient products of one block, shapes only.
 void block_dw_shapes(const gpt2_config& c, TnJobDesc* jobs) {
@@ -167,10 +176,16 @@ ScratchPlan plan_scratch(const gpt2_config& c) {
     s.col_partial = off;
     off = align_up(off + s.col_partial_elems * 4);
     {
-        // one block's grouped weight-gradient products, and the lm_head's
-        TnJobDesc blk[4];
-        block_dw_shapes(c, blk);
-        s.splitk_elems = std::max(gemm_tn_group_partial_elems(blk, 4, (int)BT),
+        // the blocks' grouped weight-gradient products (chunks of DW_GROUP_BLOCKS
+        // blocks, the last one possibly shorter), and the lm_head's
+        TnJobDesc blk[4 * DW_GROUP_BLOCKS];
+        int64_t part = 0;
+        for (int l0 = 0; l0 < c.L; l0 += DW_GROUP_BLOCKS) {
+            const int nb = std::min(DW_GROUP_BLOCKS, c.L - l0);
+            for (int k = 0; k < nb; ++k) block_dw_shapes(c, blk + 4 * k);
+            part = std::max(part, gemm_tn_group_partial_elems(blk, 4 * nb, (int)BT));
+        }
+        s.splitk_elems = std::max(part,
                                   gemm_tn_partial_elems((int)BT, c.Vp, (int)C));
     }
     s.splitk = off;
@@ -340,19 +355,6 @@ TnJobDesc block_dw_job(gpt2_handle* h, int l, int which, const uint16_t* d_out, 
     }
 }
 
-// Whether the backward launches the weight gradients of two consecutive blocks
-// together: when one block's products are too few tiles to fill the CUs (they
-// would be split over tokens, with fp32 partials and a reduce) and two blocks'
-// products fill them without a split.
-bool pair_block_dw(const gpt2_config& c) {
-    if (c.L < 2) return false;
-    TnJobDesc j[8];
-    block_dw_shapes(c, j);
-    block_dw_shapes(c, j + 4);
-    const int BT = c.B * c.T;
-    return gemm_tn_group_partial_elems(j, 4, BT) > 0 && gemm_tn_group_partial_elems(j, 8, BT) == 0;
-}
-
 int run_backward(gpt2_handle* h, hipStream_t s) {
     const gpt2_config& c = h->cfg;
     const int BT = c.B * c.T, C = c.C;
@@ -360,18 +362,7 @@ int run_backward(gpt2_handle* h, hipStream_t s) {
     float* colp = (float*)(h->S() + h->scr.col_partial);
     float* splitk = (float*)(h->S() + h->scr.splitk);
     const int64_t splitk_n = h->scr.splitk_elems;
-    // Residual-stream gradients rotate through NR buffers: a block reads the one at
-    // its output and writes the ones at x_mid and at its input.  When the weight
-    // gradients of two blocks are launched together, the first block's output and
-    // x_mid gradients, dpre and dqkv must outlive the second block's backward: five
-    // residual buffers and a second dpre / dqkv then keep them.
-    const bool pair = pair_block_dw(c);
-    const int NR = pair ? 5 : 3;
-    uint16_t* d_res[5];
-    for (int i = 0; i < 5; ++i) d_res[i] = h->act<uint16_t>(A.d_res[i]);
     uint16_t* d_ln = h->act<uint16_t>(A.d_ln);
-    uint16_t* d_big_buf[2] = {h->act<uint16_t>(A.d_big[0]), h->act<uint16_t>(A.d_big[1])};
-    uint16_t* d_qkv_buf[2] = {h->act<uint16_t>(A.d_qkv[0]), h->act<uint16_t>(A.d_qkv[1])};
     uint16_t* d_att = h->act<uint16_t>(A.d_att);
     uint16_t* dlogits = h->act<uint16_t>(A.logits);
 
@@ -379,19 +370,19 @@ int run_backward(gpt2_handle* h, hipStream_t s) {
     HIPCHK(launch_gemm_nt(dlogits, c.Vp, h->WT(h->i_wte()), c.Vp, BT, C, c.Vp, nullptr, nullptr, 0, d_ln, C, s));
     HIPCHK(launch_gemm_tn_acc(dlogits, c.Vp, h->act<uint16_t>(A.lnf), C, BT, c.Vp, C, h->G(h->i_wte()), nullptr,
                               splitk, splitk_n, s));
-    int ri = 0;
+    // final LN: the last block's output gradient
     HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(A.xfinal), d_ln, h->P(h->i_lnf(0)), h->act<float>(A.meanf),
-                                h->act<float>(A.rstdf), d_res[ri], d_res[ri], 0, h->G(h->i_lnf(0)),
-                                h->G(h->i_lnf(1)), colp, BT, C, s));
-    TnJobDesc jobs[8];
-    int pending = 0;  // products of a block waiting for its pair
+                                h->act<float>(A.rstdf), h->act<uint16_t>(A.d_out[c.L - 1]),
+                                h->act<uint16_t>(A.d_out[c.L - 1]), 0, h->G(h->i_lnf(0)), h->G(h->i_lnf(1)), colp, BT,
+                                C, s));
+    std::vector<TnJobDesc> jobs(4 * (size_t)c.L);
     for (int l = c.L - 1; l >= 0; --l) {
         const LayerActs& la = A.layer[l];
-        uint16_t* d_out = d_res[ri];             // gradient at the block output
-        uint16_t* d_mid = d_res[(ri + 1) % NR];  // at x_mid
-        uint16_t* d_in = d_res[(ri + 2) % NR];   // at the block input
-        uint16_t* d_big = d_big_buf[pending ? 1 : 0];
-        uint16_t* d_qkv = d_qkv_buf[pending ? 1 : 0];
+        uint16_t* d_out = h->act<uint16_t>(A.d_out[l]);                       // gradient at the block output
+        uint16_t* d_mid = h->act<uint16_t>(A.d_mid[l]);                       // at x_mid
+        uint16_t* d_in = h->act<uint16_t>(l > 0 ? A.d_out[l - 1] : A.d_in0);  // at the block input
+        uint16_t* d_big = h->act<uint16_t>(A.d_big[l]);
+        uint16_t* d_qkv = h->act<uint16_t>(A.d_qkv[l]);
         // FC-proj input gradient, taken through GELU in the epilogue: d_big = dpre
         HIPCHK(launch_gemm_nt_dgelu(d_out, C, h->WT(h->i_mat(l, 3)), C, BT, 4 * C, C, h->act<uint16_t>(la.pre), d_big,
                                     4 * C, s));
@@ -412,17 +403,14 @@ int run_backward(gpt2_handle* h, hipStream_t s) {
         HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(la.x), d_ln, h->P(h->i_vec(l, 0)), h->act<float>(la.mean1),
                                     h->act<float>(la.rstd1), d_mid, d_in, 1, h->G(h->i_vec(l, 0)),
                                     h->G(h->i_vec(l, 1)), colp, BT, C, s));
-        // the block's weight and bias gradients (with the previous block's when paired)
-        for (int k = 0; k < 4; ++k) jobs[pending + k] = block_dw_job(h, l, k, d_out, d_mid, d_big, d_qkv);
-        pending += 4;
-        if (!pair || pending == 8) {
-            HIPCHK(launch_gemm_tn_group(jobs, pending, BT, splitk, splitk_n, s));
-            pending = 0;
-        }
-        ri = (ri + 2) % NR;
+        for (int k = 0; k < 4; ++k) jobs[4 * (size_t)l + k] = block_dw_job(h, l, k, d_out, d_mid, d_big, d_qkv);
     }
-    if (pending) HIPCHK(launch_gemm_tn_group(jobs, pending, BT, splitk, splitk_n, s));
-    HIPCHK(launch_embedding_bwd(h->last_tok, d_res[ri], h->G(h->i_wte()), h->G(h->i_wpe()), c.B, c.T, C, c.V,
+    // all blocks' weight and bias gradients, in grouped calls of up to DW_GROUP_BLOCKS blocks
+    for (int l0 = 0; l0 < c.L; l0 += DW_GROUP_BLOCKS) {
+        const int nb = std::min(DW_GROUP_BLOCKS, c.L - l0);
+        HIPCHK(launch_gemm_tn_group(jobs.data() + 4 * (size_t)l0, 4 * nb, BT, splitk, splitk_n, s));
+    }
+    HIPCHK(launch_embedding_bwd(h->last_tok, h->act<uint16_t>(A.d_in0), h->G(h->i_wte()), h->G(h->i_wpe()), c.B, c.T, C, c.V,
                                 (int32_t*)(h->S() + h->scr.emb_work), h->scr.emb_work_elems, s));
     return GPT2_OK;
 }

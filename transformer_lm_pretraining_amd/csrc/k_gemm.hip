@@ -18,6 +18,7 @@
 // grouped tile order.  Weight-gradient GEMMs split the token reduction (uneven
 // splits allowed) to fill the 256 CUs; the fp32 partials are summed into dW by
 // a second kernel.
+#include <algorithm>
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
@@ -607,7 +608,7 @@ __device__ __forceinline__ void lds_dma16_asm(const uint16_t* src, uint16_t* dst
 }
 
 // One weight-gradient product of a grouped launch.
-constexpr int TN_MAX_JOBS = 8;
+constexpr int TN_MAX_JOBS = 48;
 struct TnJob {
     const uint16_t* A;  // dY [tokens][M] (row stride lda)
     const uint16_t* B;  // X  [tokens][N] (row stride ldb)
@@ -896,6 +897,39 @@ int tn_group_splits(int64_t tiles, int nk) {
     return best;
 }
 
+// A group of products whose tiles fill whole passes over the CUs except for a
+// mostly idle last pass: the smallest products that cover that remainder run
+// as a second launch split over tokens (with fp32 partials and a reduce), the
+// rest as full passes.  head / tail receive job indices in their given order.
+bool tn_group_tail_plan(const TnJobDesc* jobs, int n, int nk, int* head, int* nh, int* tail, int* nt,
+                        int* tail_splits) {
+    if (n < 2) return false;
+    int64_t t[TN_MAX_JOBS], T = 0;
+    for (int j = 0; j < n; ++j) {
+        t[j] = cdiv(jobs[j].N, BIG) * cdiv(jobs[j].K, BIG);
+        T += t[j];
+    }
+    const int64_t r = T % NUM_CU;
+    if (T < NUM_CU || r == 0 || r * 5 >= NUM_CU * 4) return false;
+    int order[TN_MAX_JOBS];
+    for (int j = 0; j < n; ++j) order[j] = j;
+    std::stable_sort(order, order + n, [&](int a, int b) { return t[a] < t[b]; });
+    int64_t st = 0;
+    int k = 0;
+    while (k < n && st < r) st += t[order[k++]];
+    if (k >= n) return false;
+    const int sp = tn_group_splits(st, nk);
+    if (sp < 2) return false;
+    const double passes = std::ceil((double)(T - st) / NUM_CU) + std::ceil((double)(st * sp) / NUM_CU) / sp;
+    if (passes >= std::ceil((double)T / NUM_CU) - 0.25) return false;
+    bool in_tail[TN_MAX_JOBS] = {};
+    for (int i = 0; i < k; ++i) in_tail[order[i]] = true;
+    *nh = *nt = 0;
+    for (int j = 0; j < n; ++j) (in_tail[j] ? tail[(*nt)++] : head[(*nh)++]) = j;
+    *tail_splits = sp;
+    return true;
+}
+
 bool tn_pipe_ok(int M, int64_t ldy, int64_t ldx, int N, int K) {
     // 32-bit element offsets, 16-byte vectors, 256x256 tiles worth running
     return ldy % 8 == 0 && ldx % 8 == 0 && N % 8 == 0 && K % 8 == 0 && (int64_t)M * ldy < (1ll << 31) &&
@@ -1032,6 +1066,14 @@ hipError_t launch_gemm_tn_group(const TnJobDesc* jobs, int n, int M, float* part
         hipError_t e = run_tn_group(&head, 1, M, nullptr, 0, s);
         return e != hipSuccess ? e : run_tn_group(&tail, 1, M, partial, partial_elems, s);
     }
+    int hi[TN_MAX_JOBS], ti[TN_MAX_JOBS], nh = 0, nt = 0;
+    if (pipe && tn_group_tail_plan(jobs, n, M / BK, hi, &nh, ti, &nt, &tail_sp)) {
+        TnJobDesc hj[TN_MAX_JOBS], tj[TN_MAX_JOBS];
+        for (int i = 0; i < nh; ++i) hj[i] = jobs[hi[i]];
+        for (int i = 0; i < nt; ++i) tj[i] = jobs[ti[i]];
+        hipError_t e = run_tn_group(hj, nh, M, nullptr, 0, s);
+        return e != hipSuccess ? e : run_tn_group(tj, nt, M, partial, partial_elems, s);
+    }
     if (pipe && tiles >= 8) return run_tn_group(jobs, n, M, partial, partial_elems, s);
     // small or unaligned products: the generic 128x128 kernel, one job at a time
     for (int j = 0; j < n; ++j) {
@@ -1049,6 +1091,12 @@ int64_t gemm_tn_group_partial_elems(const TnJobDesc* jobs, int n, int M) {
     int full_rows = 0, tail_sp = 1;
     if (n == 1 && tn_tail_plan(jobs[0].N, jobs[0].K, M / BK, &full_rows, &tail_sp))
         return (int64_t)tail_sp * (jobs[0].N - full_rows) * jobs[0].K;
+    int hi[TN_MAX_JOBS], ti[TN_MAX_JOBS], nh = 0, nt = 0;
+    if (n <= TN_MAX_JOBS && tn_group_tail_plan(jobs, n, M / BK, hi, &nh, ti, &nt, &tail_sp)) {
+        int64_t e = 0;
+        for (int i = 0; i < nt; ++i) e += (int64_t)jobs[ti[i]].N * jobs[ti[i]].K;
+        return tail_sp * e;
+    }
     int64_t tiles = 0, elems = 0;
     for (int j = 0; j < n; ++j) {
         tiles += cdiv(jobs[j].N, BIG) * cdiv(jobs[j].K, BIG);

@@ -32,7 +32,10 @@ struct TnJobDesc {
     float* dW;
     float* db;
 };
-// Up to 8 products over the same M tokens in one launch (+ one reduce when split).
+// Up to 48 products over the same M tokens in one launch (+ one reduce when split;
+// a mostly idle last pass is avoided by running the smallest products as a second,
+// token-split launch).
+constexpr int TN_GROUP_MAX = 48;
 hipError_t launch_gemm_tn_group(const TnJobDesc* jobs, int n, int M, float* partial, int64_t partial_elems,
                                 hipStream_t s);
 int64_t gemm_tn_group_partial_elems(const TnJobDesc* jobs, int n, int M);
