@@ -69,8 +69,10 @@ int gpt2k_bias_gelu_bwd(const uint16_t* pre, const uint16_t* dg, uint16_t* dpre,
  * Linear-layer GEMMs on bf16 MFMA with fp32 accumulation.
  *  gpt2k_gemm_nt: out[M, N] = A[M, K] . B[N, K]^T (+ bias[N]) (+ res[M, N]),
  *    bf16 out/res, fp32 bias; bias/res may be NULL.  K % 64 == 0.
- *  gpt2k_gemm_nt_gelu: pre = A . B^T + bias, g = GELU(pre), both bf16 [M, N].
- *  gpt2k_gemm_nt_dgelu: out = (A . B^T) * GELU'(pre) (bf16 pre, out [M, N]):
+ *  gpt2k_gemm_nt_gelu: with pre = A . B^T + bias rounded to bf16, writes
+ *    g = GELU(pre) and gprime = GELU'(pre), both bf16 [M, N] (the backward
+ *    needs only the derivative of the pre-activation, so it is stored instead).
+ *  gpt2k_gemm_nt_dgelu: out = (A . B^T) * gprime (bf16 gprime, out [M, N]):
  *    the input gradient of the MLP projection taken through the GELU.
  *  gpt2k_gemm_tn_acc: dW[N, K] += sum_m dY[m, n] X[m, k] (fp32 dW, bf16
  *    dY [M, N] and X [M, K]) and, if db != NULL, db[n] += sum_m dY[m, n]
@@ -79,9 +81,9 @@ int gpt2k_bias_gelu_bwd(const uint16_t* pre, const uint16_t* dg, uint16_t* dpre,
  */
 int gpt2k_gemm_nt(const uint16_t* A, const uint16_t* B, const float* bias, const uint16_t* res, uint16_t* out,
                   int64_t M, int64_t N, int64_t K, hipStream_t stream);
-int gpt2k_gemm_nt_gelu(const uint16_t* A, const uint16_t* B, const float* bias, uint16_t* pre, uint16_t* g,
+int gpt2k_gemm_nt_gelu(const uint16_t* A, const uint16_t* B, const float* bias, uint16_t* gprime, uint16_t* g,
                        int64_t M, int64_t N, int64_t K, hipStream_t stream);
-int gpt2k_gemm_nt_dgelu(const uint16_t* A, const uint16_t* B, const uint16_t* pre, uint16_t* out, int64_t M,
+int gpt2k_gemm_nt_dgelu(const uint16_t* A, const uint16_t* B, const uint16_t* gprime, uint16_t* out, int64_t M,
                         int64_t N, int64_t K, hipStream_t stream);
 int gpt2k_gemm_tn_acc(const uint16_t* dY, const uint16_t* X, float* dW, float* db, void* scratch,
                       int64_t scratch_bytes, int64_t M, int64_t N, int64_t K, hipStream_t stream);

@@ -163,19 +163,22 @@ def test_gemm_nt_parity(gpu_lib, M, N, K):
     assert rel_l2(host(out), ref + bias + res) <= 5e-3
 
 
-def test_gemm_nt_gelu_parity(gpu_lib):
+@pytest.mark.parametrize("M", [333, 4000])  # small-shape kernel; 256x256-tile kernel with a ragged last row tile
+def test_gemm_nt_gelu_parity(gpu_lib, M):
     import torch
     from transformer_lm_pretraining_amd import lib
-    M, N, K = 333, 3072, 768
+    N, K = 3072, 768
     say("gemm_nt_gelu", M, N, K)
     A = bf16_round(synth.normal((M, K), seed=61))
     B = bf16_round(synth.normal((N, K), std=0.05, seed=62))
     bias = synth.normal((N,), std=0.1, seed=63).astype(np.float64)
-    pre, g = lib.gemm_nt_gelu(to_dev_bf16(A), to_dev_bf16(B), to_dev_f32(bias))
+    gprime, g = lib.gemm_nt_gelu(to_dev_bf16(A), to_dev_bf16(B), to_dev_f32(bias))
     torch.cuda.synchronize()
     ref = A @ B.T + bias
-    assert rel_l2(host(pre), ref) <= 5e-3
     assert rel_l2(host(g), ops.gelu_fwd(ref)) <= 5e-3
+    # the stored derivative of the pre-activation, GELU'(pre), for the backward
+    assert rel_l2(host(gprime), ops.gelu_grad(ref)) <= 5e-3
+    assert np.max(np.abs(host(gprime) - ops.gelu_grad(ref))) <= 2e-2
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 128, 128), (19456, 768, 768), (2048, 50304, 768), (4096, 768, 3072)])
@@ -202,15 +205,17 @@ def test_gemm_tn_acc_parity(gpu_lib, M, N, K):
     assert rel_l2(host(dW2), ref) <= 1e-4
 
 
-def test_gemm_nt_dgelu_parity(gpu_lib):
+@pytest.mark.parametrize("M", [515, 4000])
+def test_gemm_nt_dgelu_parity(gpu_lib, M):
     import torch
     from transformer_lm_pretraining_amd import lib
-    M, N, K = 515, 3072, 768
+    N, K = 3072, 768
     say("gemm_nt_dgelu", M, N, K)
     A = bf16_round(synth.normal((M, K), seed=65))
     B = bf16_round(synth.normal((N, K), std=0.05, seed=66))
     pre = bf16_round(synth.normal((M, N), seed=67))
-    out = lib.gemm_nt_dgelu(to_dev_bf16(A), to_dev_bf16(B), to_dev_bf16(pre))
+    gprime = bf16_round(ops.gelu_grad(pre))  # what the forward stores for this pre-activation
+    out = lib.gemm_nt_dgelu(to_dev_bf16(A), to_dev_bf16(B), to_dev_bf16(gprime))
     torch.cuda.synchronize()
     assert rel_l2(host(out), ops.gelu_bwd(pre, A @ B.T)) <= 5e-3
 

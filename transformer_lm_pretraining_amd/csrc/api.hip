@@ -85,7 +85,7 @@ std::vector<Tensor> tensors_of(const gpt2_config& c) {
 
 // Byte offsets of the saved activations and backward temporaries in `acts`.
 struct LayerActs {
-    int64_t x, ln1, mean1, rstd1, qkv, att, lse, xmid, ln2, mean2, rstd2, pre, gel;
+    int64_t x, ln1, mean1, rstd1, qkv, att, lse, xmid, ln2, mean2, rstd2, gprime, gel;
 };
 struct ActsPlan {
     std::vector<LayerActs> layer;
@@ -126,7 +126,7 @@ ActsPlan plan_acts(const gpt2_config& c) {
         la.ln2 = take(BT * C * 2);
         la.mean2 = take(BT * 4);
         la.rstd2 = take(BT * 4);
-        la.pre = take(BT * 4 * C * 2);
+        la.gprime = take(BT * 4 * C * 2);  // GELU'(pre), what the FC-proj backward needs of pre
         la.gel = take(BT * 4 * C * 2);
         a.layer.push_back(la);
     }
@@ -316,7 +316,7 @@ int run_forward(gpt2_handle* h, const int32_t* tok, const int32_t* tgt, float dl
                                     h->act<uint16_t>(la.ln2), h->act<float>(la.mean2), h->act<float>(la.rstd2), BT,
                                     C, s));
         HIPCHK(launch_gemm_nt_gelu(h->act<uint16_t>(la.ln2), C, h->W(h->i_mat(l, 2)), C, BT, 4 * C, C,
-                                   h->P(h->i_vec(l, 6)), h->act<uint16_t>(la.pre), h->act<uint16_t>(la.gel), 4 * C,
+                                   h->P(h->i_vec(l, 6)), h->act<uint16_t>(la.gprime), h->act<uint16_t>(la.gel), 4 * C,
                                    s));
         HIPCHK(launch_gemm_nt(h->act<uint16_t>(la.gel), 4 * C, h->W(h->i_mat(l, 3)), 4 * C, BT, C, 4 * C,
                               h->P(h->i_vec(l, 7)), h->act<uint16_t>(la.xmid), C, h->act<uint16_t>(xnext), C, s));
@@ -383,8 +383,8 @@ int run_backward(gpt2_handle* h, hipStream_t s) {
         uint16_t* d_in = h->act<uint16_t>(l > 0 ? A.d_out[l - 1] : A.d_in0);  // at the block input
         uint16_t* d_big = h->act<uint16_t>(A.d_big[l]);
         uint16_t* d_qkv = h->act<uint16_t>(A.d_qkv[l]);
-        // FC-proj input gradient, taken through GELU in the epilogue: d_big = dpre
-        HIPCHK(launch_gemm_nt_dgelu(d_out, C, h->WT(h->i_mat(l, 3)), C, BT, 4 * C, C, h->act<uint16_t>(la.pre), d_big,
+        // FC-proj input gradient, taken through GELU in the epilogue: d_big = dpre = dgel * GELU'(pre)
+        HIPCHK(launch_gemm_nt_dgelu(d_out, C, h->WT(h->i_mat(l, 3)), C, BT, 4 * C, C, h->act<uint16_t>(la.gprime), d_big,
                                     4 * C, s));
         // FC input gradient, then LN2: d_mid = d_out + LN2'(d_ln)
         HIPCHK(launch_gemm_nt(d_big, 4 * C, h->WT(h->i_mat(l, 2)), 4 * C, BT, C, 4 * C, nullptr, nullptr, 0, d_ln, C,
@@ -739,19 +739,19 @@ int gpt2k_gemm_nt(const uint16_t* A, const uint16_t* B, const float* bias, const
     return GPT2_OK;
 }
 
-int gpt2k_gemm_nt_gelu(const uint16_t* A, const uint16_t* B, const float* bias, uint16_t* pre, uint16_t* g,
+int gpt2k_gemm_nt_gelu(const uint16_t* A, const uint16_t* B, const float* bias, uint16_t* gprime, uint16_t* g,
                        int64_t M, int64_t N, int64_t K, hipStream_t s) {
-    if (!A || !B || !bias || !pre || !g || M < 1 || N < 1 || K < 64 || K % 64 || N % 8 || M > INT32_MAX)
+    if (!A || !B || !bias || !gprime || !g || M < 1 || N < 1 || K < 64 || K % 64 || N % 8 || M > INT32_MAX)
         return GPT2_E_INVALID;
-    KCHK(launch_gemm_nt_gelu(A, K, B, K, (int)M, (int)N, (int)K, bias, pre, g, N, s));
+    KCHK(launch_gemm_nt_gelu(A, K, B, K, (int)M, (int)N, (int)K, bias, gprime, g, N, s));
     return GPT2_OK;
 }
 
-int gpt2k_gemm_nt_dgelu(const uint16_t* A, const uint16_t* B, const uint16_t* pre, uint16_t* out, int64_t M,
+int gpt2k_gemm_nt_dgelu(const uint16_t* A, const uint16_t* B, const uint16_t* gprime, uint16_t* out, int64_t M,
                         int64_t N, int64_t K, hipStream_t s) {
-    if (!A || !B || !pre || !out || M < 1 || N < 1 || K < 64 || K % 64 || N % 8 || M > INT32_MAX)
+    if (!A || !B || !gprime || !out || M < 1 || N < 1 || K < 64 || K % 64 || N % 8 || M > INT32_MAX)
         return GPT2_E_INVALID;
-    KCHK(launch_gemm_nt_dgelu(A, K, B, K, (int)M, (int)N, (int)K, pre, out, N, s));
+    KCHK(launch_gemm_nt_dgelu(A, K, B, K, (int)M, (int)N, (int)K, gprime, out, N, s));
     return GPT2_OK;
 }
 

@@ -103,5 +103,13 @@ __device__ __forceinline__ float gelu_grad_f(float x) {
     const float d = fmaf(2.0f * 0.7978845608028654f * 3.0f * 0.044715f, x2, 2.0f * 0.7978845608028654f);
     return fmaf(x * s * (1.0f - s), d, s);
 }
+// Both at once (one exponential and one reciprocal).
+__device__ __forceinline__ void gelu_and_grad_f(float x, float& g, float& gp) {
+    const float x2 = x * x;
+    const float s = gelu_sigmoid(x, x2);
+    const float d = fmaf(2.0f * 0.7978845608028654f * 3.0f * 0.044715f, x2, 2.0f * 0.7978845608028654f);
+    g = x * s;
+    gp = fmaf(g * (1.0f - s), d, s);
+}
 
 __host__ __device__ static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -44,7 +44,7 @@ struct GemmParams {
     int tiles_m, tiles_n;
     int band;          // tile order: row tiles per band, 0 = round-robin bands of GROUP_M (see nt_tile)
     const float* bias;
-    const uint16_t* res;   // residual (EPI_BF16 / EPI_BF16R) or pre-activation (EPI_DGELU)
+    const uint16_t* res;   // residual (EPI_BF16 / EPI_BF16R) or GELU'(pre-activation) (EPI_DGELU)
     int64_t ldr;
     uint16_t* out;
     uint16_t* out2;
@@ -282,11 +282,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmParams p) {
                     if (p.res) x += bf2f(p.res[(int64_t)row * p.ldr + col]);
                     p.out[(int64_t)row * p.ldo + col] = f2bf(x);
                 } else if constexpr (EPI == EPI_GELU) {
-                    const uint16_t pre = f2bf(x + bcol);
-                    p.out[(int64_t)row * p.ldo + col] = pre;
-                    p.out2[(int64_t)row * p.ldo + col] = f2bf(gelu_f(bf2f(pre)));
+                    float g, gp;
+                    gelu_and_grad_f(bf2f(f2bf(x + bcol)), g, gp);
+                    p.out[(int64_t)row * p.ldo + col] = f2bf(gp);
+                    p.out2[(int64_t)row * p.ldo + col] = f2bf(g);
                 } else if constexpr (EPI == EPI_DGELU) {
-                    x *= gelu_grad_f(bf2f(p.res[(int64_t)row * p.ldr + col]));
+                    x *= bf2f(p.res[(int64_t)row * p.ldr + col]);
                     p.out[(int64_t)row * p.ldo + col] = f2bf(x);
                 } else if constexpr (EPI == EPI_F32_ACC) {
                     p.outf[(int64_t)row * p.ldf + col] += x;
@@ -547,16 +548,23 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_w8_kernel(GemmParams p) {
             for (int e = 0; e < 4; ++e) w[e] = pack_bf2(bflo(w[e]) + bflo(r[e]), bfhi(w[e]) + bfhi(r[e]));
             *(u32x4*)(p.out + o) = w;
         } else if constexpr (EPI == EPI_GELU) {
-            u32x4 gv;
+            // w holds the bf16 pre-activation: GELU goes to out2, GELU' to out
+            u32x4 gv, gd;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) gv[e] = pack_bf2(gelu_f(bflo(w[e])), gelu_f(bfhi(w[e])));
-            *(u32x4*)(p.out + o) = w;
+            for (int e = 0; e < 4; ++e) {
+                float g0, d0, g1, d1;
+                gelu_and_grad_f(bflo(w[e]), g0, d0);
+                gelu_and_grad_f(bfhi(w[e]), g1, d1);
+                gv[e] = pack_bf2(g0, g1);
+                gd[e] = pack_bf2(d0, d1);
+            }
+            *(u32x4*)(p.out + o) = gd;
             *(u32x4*)(p.out2 + o) = gv;
-        } else {  // EPI_DGELU
+        } else {  // EPI_DGELU: times the stored GELU'
             const u32x4 pr = pin[it];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                w[e] = pack_bf2(bflo(w[e]) * gelu_grad_f(bflo(pr[e])), bfhi(w[e]) * gelu_grad_f(bfhi(pr[e])));
+                w[e] = pack_bf2(bflo(w[e]) * bflo(pr[e]), bfhi(w[e]) * bfhi(pr[e]));
             *(u32x4*)(p.out + o) = w;
         }
     };
@@ -1021,18 +1029,18 @@ hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int
 }
 
 hipError_t launch_gemm_nt_gelu(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M, int N, int K,
-                               const float* bias, uint16_t* pre, uint16_t* g, int64_t ldo, hipStream_t s) {
+                               const float* bias, uint16_t* gprime, uint16_t* g, int64_t ldo, hipStream_t s) {
     GemmParams p{};
     p.A = A; p.B = B; p.lda = lda; p.ldb = ldb; p.M = M; p.N = N; p.nk_total = K / BK;
-    p.bias = bias; p.out = pre; p.out2 = g; p.ldo = ldo;
+    p.bias = bias; p.out = gprime; p.out2 = g; p.ldo = ldo;
     return run_nt<EPI_GELU>(p, s);
 }
 
 hipError_t launch_gemm_nt_dgelu(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M, int N, int K,
-                                const uint16_t* pre, uint16_t* out, int64_t ldo, hipStream_t s) {
+                                const uint16_t* gprime, uint16_t* out, int64_t ldo, hipStream_t s) {
     GemmParams p{};
     p.A = A; p.B = B; p.lda = lda; p.ldb = ldb; p.M = M; p.N = N; p.nk_total = K / BK;
-    p.res = pre; p.ldr = ldo; p.out = out; p.ldo = ldo;
+    p.res = gprime; p.ldr = ldo; p.out = out; p.ldo = ldo;
     return run_nt<EPI_DGELU>(p, s);
 }
 

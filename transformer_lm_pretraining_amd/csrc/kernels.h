@@ -11,12 +11,12 @@
 hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M, int N, int K,
                           const float* bias, const uint16_t* res, int64_t ldr, uint16_t* out, int64_t ldo,
                           hipStream_t s);
-// pre = A . B^T + bias; g = GELU(pre).
+// pre = bf16(A . B^T + bias); gprime = GELU'(pre), g = GELU(pre).
 hipError_t launch_gemm_nt_gelu(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M, int N, int K,
-                               const float* bias, uint16_t* pre, uint16_t* g, int64_t ldo, hipStream_t s);
-// out = (A . B^T) * GELU'(pre), all bf16 [M, N] with leading dim ldo.
+                               const float* bias, uint16_t* gprime, uint16_t* g, int64_t ldo, hipStream_t s);
+// out = (A . B^T) * gprime, all bf16 [M, N] with leading dim ldo.
 hipError_t launch_gemm_nt_dgelu(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M, int N, int K,
-                                const uint16_t* pre, uint16_t* out, int64_t ldo, hipStream_t s);
+                                const uint16_t* gprime, uint16_t* out, int64_t ldo, hipStream_t s);
 // dW[N,K] += sum_m dY[m,n] X[m,k]; dbias[n] += sum_m dY[m,n] if dbias != null.
 // M % 64 == 0, N % 8 == 0, K % 8 == 0.
 hipError_t launch_gemm_tn_acc(const uint16_t* dY, int64_t ldy, const uint16_t* X, int64_t ldx, int M, int N, int K,

@@ -346,22 +346,23 @@ def gemm_nt(A, B, bias=None, res=None, out=None):
 
 
 def gemm_nt_gelu(A, B, bias):
+    """Returns (GELU'(pre), GELU(pre)) with pre = A . B^T + bias in bf16."""
     import torch
     M, K = A.shape
     N = B.shape[0]
-    pre = torch.empty(M, N, dtype=torch.bfloat16, device=A.device)
-    g = torch.empty_like(pre)
-    check(load().gpt2k_gemm_nt_gelu(_ptr(A), _ptr(B), _ptr(bias), _ptr(pre), _ptr(g), M, N, K, _stream()),
+    gprime = torch.empty(M, N, dtype=torch.bfloat16, device=A.device)
+    g = torch.empty_like(gprime)
+    check(load().gpt2k_gemm_nt_gelu(_ptr(A), _ptr(B), _ptr(bias), _ptr(gprime), _ptr(g), M, N, K, _stream()),
           "gpt2k_gemm_nt_gelu")
-    return pre, g
+    return gprime, g
 
 
-def gemm_nt_dgelu(A, B, pre):
+def gemm_nt_dgelu(A, B, gprime):
     import torch
     M, K = A.shape
     N = B.shape[0]
     out = torch.empty(M, N, dtype=torch.bfloat16, device=A.device)
-    check(load().gpt2k_gemm_nt_dgelu(_ptr(A), _ptr(B), _ptr(pre), _ptr(out), M, N, K, _stream()),
+    check(load().gpt2k_gemm_nt_dgelu(_ptr(A), _ptr(B), _ptr(gprime), _ptr(out), M, N, K, _stream()),
           "gpt2k_gemm_nt_dgelu")
     return out
 
