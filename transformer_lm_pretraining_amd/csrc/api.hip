@@ -99,8 +99,8 @@ struct ActsPlan {
 };
 struct ScratchPlan {
     int64_t flag, loss, scale, norm;  // header slots (256 B)
-    int64_t norm_partial, col_partial, splitk, dvec, emb_work;
-    int64_t col_partial_elems, splitk_elems, emb_work_elems;
+    int64_t norm_partial, col_partial, splitk, dvec, emb_work, ln_partial;
+    int64_t col_partial_elems, splitk_elems, emb_work_elems, ln_slot_elems;
     int64_t total;
 };
 
@@ -175,6 +175,10 @@ ScratchPlan plan_scratch(const gpt2_config& c) {
                                     colsum_partial_elems(BT, 3 * c.C)});
     s.col_partial = off;
     off = align_up(off + s.col_partial_elems * 4);
+    // column partials of every LayerNorm backward of a step (folded once at its end)
+    s.ln_slot_elems = layernorm_bwd_partial_elems(BT, c.C);
+    s.ln_partial = off;
+    off = align_up(off + s.ln_slot_elems * (2 * c.L + 1) * 4);
     {
         // the blocks' grouped weight-gradient products (chunks of DW_GROUP_BLOCKS
         // blocks, the last one possibly shorter), and the lm_head's
@@ -359,7 +363,6 @@ int run_backward(gpt2_handle* h, hipStream_t s) {
     const gpt2_config& c = h->cfg;
     const int BT = c.B * c.T, C = c.C;
     const ActsPlan& A = h->acts;
-    float* colp = (float*)(h->S() + h->scr.col_partial);
     float* splitk = (float*)(h->S() + h->scr.splitk);
     const int64_t splitk_n = h->scr.splitk_elems;
     uint16_t* d_ln = h->act<uint16_t>(A.d_ln);
@@ -371,10 +374,20 @@ int run_backward(gpt2_handle* h, hipStream_t s) {
     HIPCHK(launch_gemm_tn_acc(dlogits, c.Vp, h->act<uint16_t>(A.lnf), C, BT, c.Vp, C, h->G(h->i_wte()), nullptr,
                               splitk, splitk_n, s));
     // final LN: the last block's output gradient
+    // LayerNorm parameter gradients: each backward leaves its column partials in
+    // slot k of ln_partial (dw[k], db[k] are their targets); one fold at the end
+    float* lnp = (float*)(h->S() + h->scr.ln_partial);
+    const int64_t lns = h->scr.ln_slot_elems;
+    std::vector<float*> ln_dw, ln_db;
+    auto ln_slot = [&](int iw, int ib) {
+        ln_dw.push_back(h->G(iw));
+        ln_db.push_back(h->G(ib));
+        return lnp + (int64_t)(ln_dw.size() - 1) * lns;
+    };
     HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(A.xfinal), d_ln, h->P(h->i_lnf(0)), h->act<float>(A.meanf),
                                 h->act<float>(A.rstdf), h->act<uint16_t>(A.d_out[c.L - 1]),
-                                h->act<uint16_t>(A.d_out[c.L - 1]), 0, h->G(h->i_lnf(0)), h->G(h->i_lnf(1)), colp, BT,
-                                C, s));
+                                h->act<uint16_t>(A.d_out[c.L - 1]), 0, nullptr, nullptr,
+                                ln_slot(h->i_lnf(0), h->i_lnf(1)), BT, C, s));
     std::vector<TnJobDesc> jobs(4 * (size_t)c.L);
     for (int l = c.L - 1; l >= 0; --l) {
         const LayerActs& la = A.layer[l];
@@ -390,8 +403,8 @@ int run_backward(gpt2_handle* h, hipStream_t s) {
         HIPCHK(launch_gemm_nt(d_big, 4 * C, h->WT(h->i_mat(l, 2)), 4 * C, BT, C, 4 * C, nullptr, nullptr, 0, d_ln, C,
                               s));
         HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(la.xmid), d_ln, h->P(h->i_vec(l, 4)), h->act<float>(la.mean2),
-                                    h->act<float>(la.rstd2), d_out, d_mid, 1, h->G(h->i_vec(l, 4)),
-                                    h->G(h->i_vec(l, 5)), colp, BT, C, s));
+                                    h->act<float>(la.rstd2), d_out, d_mid, 1, nullptr, nullptr,
+                                    ln_slot(h->i_vec(l, 4), h->i_vec(l, 5)), BT, C, s));
         // attention projection input gradient, attention, QKV input gradient
         HIPCHK(launch_gemm_nt(d_mid, C, h->WT(h->i_mat(l, 1)), C, BT, C, C, nullptr, nullptr, 0, d_att, C, s));
         HIPCHK(launch_attention_bwd(h->act<uint16_t>(la.qkv), h->act<uint16_t>(la.att), d_att,
@@ -401,14 +414,18 @@ int run_backward(gpt2_handle* h, hipStream_t s) {
                               s));
         // LN1: d_in = d_mid + LN1'(d_ln)
         HIPCHK(launch_layernorm_bwd(h->act<uint16_t>(la.x), d_ln, h->P(h->i_vec(l, 0)), h->act<float>(la.mean1),
-                                    h->act<float>(la.rstd1), d_mid, d_in, 1, h->G(h->i_vec(l, 0)),
-                                    h->G(h->i_vec(l, 1)), colp, BT, C, s));
+                                    h->act<float>(la.rstd1), d_mid, d_in, 1, nullptr, nullptr,
+                                    ln_slot(h->i_vec(l, 0), h->i_vec(l, 1)), BT, C, s));
         for (int k = 0; k < 4; ++k) jobs[4 * (size_t)l + k] = block_dw_job(h, l, k, d_out, d_mid, d_big, d_qkv);
     }
     // all blocks' weight and bias gradients, in grouped calls of up to DW_GROUP_BLOCKS blocks
     for (int l0 = 0; l0 < c.L; l0 += DW_GROUP_BLOCKS) {
         const int nb = std::min(DW_GROUP_BLOCKS, c.L - l0);
         HIPCHK(launch_gemm_tn_group(jobs.data() + 4 * (size_t)l0, 4 * nb, BT, splitk, splitk_n, s));
+    }
+    for (int k0 = 0; k0 < (int)ln_dw.size(); k0 += LN_FOLD_MAX) {
+        const int n = std::min(LN_FOLD_MAX, (int)ln_dw.size() - k0);
+        HIPCHK(launch_layernorm_fold(lnp + (int64_t)k0 * lns, lns, n, ln_dw.data() + k0, ln_db.data() + k0, BT, C, s));
     }
     HIPCHK(launch_embedding_bwd(h->last_tok, h->act<uint16_t>(A.d_in0), h->G(h->i_wte()), h->G(h->i_wpe()), c.B, c.T, C, c.V,
                                 (int32_t*)(h->S() + h->scr.emb_work), h->scr.emb_work_elems, s));

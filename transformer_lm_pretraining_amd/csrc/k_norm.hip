@@ -30,6 +30,8 @@ struct Vec<4> {
     __device__ static T pack(const float* f) { return T{pack_bf2(f[0], f[1]), pack_bf2(f[2], f[3])}; }
 };
 
+// Each wave walks rows with a grid stride, with w and b in registers and the
+// next row's load in flight while the current row is normalised.
 template <int VEC, int NV>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(const uint16_t* __restrict__ x, const float* __restrict__ w,
                                                      const float* __restrict__ b, uint16_t* __restrict__ y,
@@ -38,42 +40,65 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const uint16_t* __restrict_
     constexpr int C = NV * 64 * VEC;
     typedef typename Vec<VEC>::T VT;
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
-    if (row >= rows) return;
-    const VT* xr = (const VT*)(x + row * C);
-    float v[NV][VEC];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) Vec<VEC>::unpack(xr[j * 64 + lane], v[j]);
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < NV; ++j)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) s += v[j][e];
-    const float mean = wave_sum(s) * (1.0f / C);
-    float q = 0.f;
+    float wv[NV][VEC], bv[NV][VEC];
 #pragma unroll
     for (int j = 0; j < NV; ++j)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            float d = v[j][e] - mean;
-            q += d * d;
+            wv[j][e] = w[(j * 64 + lane) * VEC + e];
+            bv[j][e] = b[(j * 64 + lane) * VEC + e];
         }
-    const float var = wave_sum(q) * (1.0f / C);
-    const float rstd = 1.0f / sqrtf(var + LN_EPS);
-    VT* yr = (VT*)(y + row * C);
+    auto load = [&](int64_t row, VT* xv) {
+        const VT* xr = (const VT*)(x + row * C);
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        float o[VEC];
+        for (int j = 0; j < NV; ++j) xv[j] = xr[j * 64 + lane];
+    };
+    auto compute = [&](int64_t row, const VT* xv) {
+        float v[NV][VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            int c = (j * 64 + lane) * VEC + e;
-            o[e] = (v[j][e] - mean) * rstd * w[c] + b[c];
+        for (int j = 0; j < NV; ++j) Vec<VEC>::unpack(xv[j], v[j]);
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) s += v[j][e];
+        const float mean = wave_sum(s) * (1.0f / C);
+        float q = 0.f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const float d = v[j][e] - mean;
+                q += d * d;
+            }
+        const float var = wave_sum(q) * (1.0f / C);
+        const float rstd = 1.0f / sqrtf(var + LN_EPS);
+        VT* yr = (VT*)(y + row * C);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            float o[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) o[e] = (v[j][e] - mean) * rstd * wv[j][e] + bv[j][e];
+            yr[j * 64 + lane] = Vec<VEC>::pack(o);
         }
-        yr[j * 64 + lane] = Vec<VEC>::pack(o);
-    }
-    if (lane == 0) {
-        mean_out[row] = mean;
-        rstd_out[row] = rstd;
+        if (lane == 0) {
+            mean_out[row] = mean;
+            rstd_out[row] = rstd;
+        }
+    };
+    const int64_t stride = (int64_t)gridDim.x * ROWS_PER_BLOCK;
+    int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+    VT xa[NV], xb[NV];
+    if (row < rows) load(row, xa);
+    while (row < rows) {
+        const int64_t r1 = row + stride;
+        if (r1 < rows) load(r1, xb);
+        compute(row, xa);
+        if (r1 >= rows) break;
+        const int64_t r2 = r1 + stride;
+        if (r2 < rows) load(r2, xa);
+        compute(r1, xb);
+        row = r2;
     }
 }
 
@@ -203,14 +228,41 @@ __global__ __launch_bounds__(256) void fold_partials_kernel(const float* __restr
         unsafeAtomicAdd(out1 + c - C, t);
 }
 
+// The same fold for several LayerNorms at once: z-slice z sums partial slot z
+// into dw[z], db[z].
+struct LnFoldSet {
+    float* dw[LN_FOLD_MAX];
+    float* db[LN_FOLD_MAX];
+};
+__global__ __launch_bounds__(256) void fold_partials_many_kernel(const float* __restrict__ partial, int64_t slot_elems,
+                                                                 int nblocks, int C, LnFoldSet set) {
+    const int z = blockIdx.z;
+    const float* part = partial + (int64_t)z * slot_elems;
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= 2 * C) return;
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int b = blockIdx.y;
+    for (; b + 7 * FOLD_SEGS < nblocks; b += 8 * FOLD_SEGS) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s[u] += part[(int64_t)(b + u * FOLD_SEGS) * 2 * C + c];
+    }
+    for (; b < nblocks; b += FOLD_SEGS) s[0] += part[(int64_t)b * 2 * C + c];
+    const float t = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+    if (c < C)
+        unsafeAtomicAdd(set.dw[z] + c, t);
+    else
+        unsafeAtomicAdd(set.db[z] + c - C, t);
+}
+
 int ln_blocks(int64_t rows) { return (int)std::min<int64_t>(768, cdiv(rows, ROWS_PER_BLOCK)); }
 
 template <int VEC, int NV>
 hipError_t ln_fwd_t(const uint16_t* x, const float* w, const float* b, uint16_t* y, float* mean, float* rstd,
                     int64_t rows, hipStream_t s) {
     constexpr int C = NV * 64 * VEC;
-    PROF_LAUNCH(KC_LN_FWD, 4.0 * rows * C, s, hipLaunchKernelGGL((ln_fwd_kernel<VEC, NV>), dim3(cdiv(rows, ROWS_PER_BLOCK)), dim3(256), 0, s, x, w, b, y, mean,
-                       rstd, rows));
+    PROF_LAUNCH(KC_LN_FWD, 4.0 * rows * C, s,
+                hipLaunchKernelGGL((ln_fwd_kernel<VEC, NV>), dim3(ln_blocks(rows)), dim3(256), 0, s, x, w, b, y, mean,
+                                   rstd, rows));
     return hipGetLastError();
 }
 
@@ -224,7 +276,7 @@ hipError_t ln_bwd_t(const uint16_t* x, const uint16_t* dy, const float* w, const
     PROF_LAUNCH(KC_LN_BWD, 2.0 * rows * C * (accumulate ? 4 : 3), s, hipLaunchKernelGGL((ln_bwd_kernel<VEC, NV>), dim3(blocks), dim3(256), 0, s, x, dy, w, mean, rstd, dres_in, dres,
                        accumulate, partial, rows));
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || dw == nullptr) return e;  // no dw: the partials are folded later
     PROF_LAUNCH(KC_FOLD, 8.0 * blocks * C, s,
                 hipLaunchKernelGGL(fold_partials_kernel, dim3(cdiv(2 * C, 256), FOLD_SEGS), dim3(256), 0, s, partial,
                                    blocks, C, dw, db));
@@ -270,6 +322,21 @@ hipError_t launch_layernorm_bwd(const uint16_t* x, const uint16_t* dy, const flo
 #undef X
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_layernorm_fold(const float* partial, int64_t slot_elems, int nslots, float* const* dw,
+                                 float* const* db, int64_t rows, int C, hipStream_t s) {
+    if (nslots < 1 || nslots > LN_FOLD_MAX || rows <= 0) return nslots == 0 ? hipSuccess : hipErrorInvalidValue;
+    LnFoldSet set{};
+    for (int i = 0; i < nslots; ++i) {
+        set.dw[i] = dw[i];
+        set.db[i] = db[i];
+    }
+    const int blocks = ln_blocks(rows);
+    PROF_LAUNCH(KC_FOLD, 8.0 * blocks * C * nslots, s,
+                hipLaunchKernelGGL(fold_partials_many_kernel, dim3(cdiv(2 * C, 256), FOLD_SEGS, nslots), dim3(256), 0,
+                                   s, partial, slot_elems, blocks, C, set));
+    return hipGetLastError();
 }
 
 bool layernorm_supports(int C) {

@@ -46,6 +46,12 @@ bool layernorm_supports(int C);
 hipError_t launch_layernorm_fwd(const uint16_t* x, const float* w, const float* b, uint16_t* y, float* mean,
                                 float* rstd, int64_t rows, int C, hipStream_t s);
 int64_t layernorm_bwd_partial_elems(int64_t rows, int C);
+// With dw == nullptr the LayerNorm backward leaves its column partials in
+// `partial` (layernorm_bwd_partial_elems floats); launch_layernorm_fold then
+// adds slots 0..nslots-1 (slot_elems apart) into dw[i], db[i] in one launch.
+constexpr int LN_FOLD_MAX = 64;
+hipError_t launch_layernorm_fold(const float* partial, int64_t slot_elems, int nslots, float* const* dw,
+                                 float* const* db, int64_t rows, int C, hipStream_t s);
 // dres = (accumulate ? dres_in : 0) + dx; dres_in may equal dres (in place)
 hipError_t launch_layernorm_bwd(const uint16_t* x, const uint16_t* dy, const float* w, const float* mean,
                                 const float* rstd, const uint16_t* dres_in, uint16_t* dres, int accumulate,
