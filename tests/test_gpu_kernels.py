@@ -337,14 +337,18 @@ def test_embedding_parity(gpu_lib):
 def test_embedding_bwd_hot_tokens_and_invalid_ids(gpu_lib):
     """Token-table scatter at the full batch (Zipf ids: token 0 covers ~14% of rows), plus
     a batch where one id fills 300 rows (runs crossing many sorting windows) and ids
-    outside [0, V) that must be skipped."""
+    outside [0, V) that must be skipped, and a batch of 71,680 rows (two sort chunks)."""
     import torch
     from transformer_lm_pretraining_amd import lib
-    C, V, Vp = 768, 50257, 50304
-    for case in ("zipf_full", "hot_invalid"):
+    V, Vp = 50257, 50304
+    for case in ("zipf_full", "hot_invalid", "over_65535_rows"):
+        C = 128 if case == "over_65535_rows" else 768
         if case == "zipf_full":
             B, T = 19, 1024
             tok, _ = synth.micro_batches(1, B, T, V, seed=11)[0]
+        elif case == "over_65535_rows":  # the sort works on chunks of at most 65,535 rows
+            B, T = 70, 1024
+            tok, _ = synth.micro_batches(1, B, T, V, seed=14)[0]
         else:
             B, T = 2, 512
             tok = np.ascontiguousarray(synth.micro_batches(1, B, T, V, seed=12)[0][0])

@@ -250,136 +250,90 @@ __global__ __launch_bounds__(256) void embedding_fwd_kernel(const int32_t* __res
     }
 }
 
-// Token-table gradient: the rows are counting-sorted by token id (count,
-// scan, scatter), then each wave sums a window of EMB_WIN sorted rows run by
-// run.  A token occurring N times (Zipf: the most frequent id covers ~14% of a
+// Token-table gradient: the rows are counting-sorted by token id (one
+// workgroup: count, scan and scatter in LDS), then each wave sums a window of
+// EMB_WIN sorted rows run by run, for a chunk of columns.  A token occurring N times (Zipf: the most frequent id covers ~14% of a
 // batch) then costs about N / EMB_WIN additions to its table row instead of N
-// contending atomics.  The lanes of a wave that hold the same id are combined
-// before counting / claiming positions, so no counter sees more than one
-// atomic per wave.  A run that lies inside one window is the only writer of
+// contending atomics.  A run that lies inside one window is the only writer of
 // its table row and read-modify-writes it; a run that crosses a window edge
 // adds atomically.  Ids outside [0, V) are left out.
 constexpr int EMB_WIN = 32;
 
-__global__ __launch_bounds__(256) void emb_zero_kernel(int32_t* __restrict__ p, int n) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < n) p[i] = 0;
-}
-
-__global__ __launch_bounds__(256) void emb_count_kernel(const int32_t* __restrict__ tok, int64_t rows, int V,
-                                                        int32_t* __restrict__ counts) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int lane = threadIdx.x & 63;
-    const int t = i < rows ? tok[i] : -1;
-    bool active = t >= 0 && t < V;
-    while (true) {
-        const uint64_t act = __ballot(active);
-        if (act == 0) break;
-        const int leader = __ffsll((unsigned long long)act) - 1;
-        const int lt = __shfl(t, leader, WAVE);
-        const uint64_t same = __ballot(active && t == lt);
-        if (lane == leader) atomicAdd(counts + lt, (int)__popcll(same));
-        if (active && t == lt) active = false;
-    }
-}
-
-// Exclusive prefix sum of counts[0..V) into start[0..V] (start[V] = total) and
-// cursor[0..V); one workgroup, V <= 65536.  Thread tid owns the 4 counts at
-// 4096*i + 4*tid; a group of 8 such slices is loaded up front, then each
-// 4096-count slice is scanned with wavefront shuffles and a 16-entry scan of
-// the wave totals.
-__global__ __launch_bounds__(1024) void emb_scan_kernel(const int32_t* __restrict__ counts, int V,
-                                                        int32_t* __restrict__ start, int32_t* __restrict__ cursor) {
-    constexpr int GROUP = 8;
-    __shared__ int wsum[2][16];
+// Counting sort of the row ids by token in one workgroup, all in LDS: 16-bit
+// counts packed two per word (a batch has fewer than 65,536 rows), counted with
+// LDS atomics, scanned in place into start offsets, then advanced by the
+// scatter.  Writes order[] / stok[] (row index and token of each sorted
+// position) and n = number of valid rows to *nvalid.
+constexpr int EMB_SORT_THREADS = 1024;
+__global__ __launch_bounds__(EMB_SORT_THREADS) void emb_sort_kernel(const int32_t* __restrict__ tok, int rows, int V,
+                                                                    int32_t* __restrict__ order,
+                                                                    int32_t* __restrict__ stok,
+                                                                    int32_t* __restrict__ nvalid) {
+    __shared__ uint32_t cnt[32768];  // counts of token t in half (t & 1) of word t >> 1
+    __shared__ int wtot[EMB_SORT_THREADS / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int carry = 0;
-    for (int g0 = 0; g0 < V; g0 += GROUP * 4096) {
-        int c[GROUP][4];
-#pragma unroll
-        for (int i = 0; i < GROUP; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int k = g0 + i * 4096 + tid * 4 + e;
-                c[i][e] = k < V ? counts[k] : 0;
-            }
-#pragma unroll
-        for (int i = 0; i < GROUP; ++i) {
-            const int s0 = g0 + i * 4096;
-            if (s0 >= V) break;
-            const int tsum = c[i][0] + c[i][1] + c[i][2] + c[i][3];
-            int x = tsum;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(x, o, WAVE);
-                if (lane >= o) x += y;
-            }
-            if (lane == 63) wsum[i & 1][wave] = x;
-            __syncthreads();
-            int w = lane < 16 ? wsum[i & 1][lane] : 0;
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) {
-                const int y = __shfl_up(w, o, WAVE);
-                if (lane >= o) w += y;
-            }
-            const int before = __shfl(w, wave > 0 ? wave - 1 : 0, WAVE);
-            const int total = __shfl(w, 15, WAVE);
-            int run = carry + (wave > 0 ? before : 0) + x - tsum;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int k = s0 + tid * 4 + e;
-                if (k < V) {
-                    start[k] = run;
-                    cursor[k] = run;
-                }
-                run += c[i][e];
-            }
-            carry += total;
-        }
+    const int words = (V + 1) >> 1;
+    for (int i = tid; i < words; i += EMB_SORT_THREADS) cnt[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < rows; i += EMB_SORT_THREADS) {
+        const int t = tok[i];
+        if (t >= 0 && t < V) atomicAdd(&cnt[t >> 1], 1u << ((t & 1) * 16));
     }
-    if (tid == 0) start[V] = carry;
-}
-
-__global__ __launch_bounds__(256) void emb_scatter_kernel(const int32_t* __restrict__ tok, int64_t rows, int V,
-                                                          int32_t* __restrict__ cursor, int32_t* __restrict__ order,
-                                                          int32_t* __restrict__ stok) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int lane = threadIdx.x & 63;
-    const int t = i < rows ? tok[i] : -1;
-    bool active = t >= 0 && t < V;
-    while (true) {
-        const uint64_t act = __ballot(active);
-        if (act == 0) break;
-        const int leader = __ffsll((unsigned long long)act) - 1;
-        const int lt = __shfl(t, leader, WAVE);
-        const uint64_t same = __ballot(active && t == lt);
-        int base = 0;
-        if (lane == leader) base = atomicAdd(cursor + lt, (int)__popcll(same));
-        base = __shfl(base, leader, WAVE);
-        if (active && t == lt) {
-            const int pos = base + (int)__popcll(same & ((1ull << lane) - 1ull));
-            order[pos] = (int)i;
-            stok[pos] = lt;
-            active = false;
-        }
+    __syncthreads();
+    // exclusive scan over the counts: thread tid owns words [tid*per, (tid+1)*per)
+    const int per = (words + EMB_SORT_THREADS - 1) / EMB_SORT_THREADS;
+    const int w0 = min(tid * per, words), w1 = min(w0 + per, words);
+    int local = 0;
+    for (int w = w0; w < w1; ++w) local += (int)(cnt[w] & 0xffffu) + (int)(cnt[w] >> 16);
+    int x = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, WAVE);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wtot[wave] = x;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wtot[w];
+    int run = before + x - local;
+    for (int w = w0; w < w1; ++w) {
+        const uint32_t c = cnt[w];
+        const uint32_t lo = (uint32_t)run, hi = (uint32_t)(run + (int)(c & 0xffffu));
+        run = (int)hi + (int)(c >> 16);
+        cnt[w] = lo | (hi << 16);
+    }
+    if (tid == EMB_SORT_THREADS - 1) *nvalid = run;
+    __syncthreads();
+    for (int i = tid; i < rows; i += EMB_SORT_THREADS) {
+        const int t = tok[i];
+        if (t < 0 || t >= V) continue;
+        const int sh = (t & 1) * 16;
+        const int pos = (int)((atomicAdd(&cnt[t >> 1], 1u << sh) >> sh) & 0xffffu);
+        order[pos] = i;
+        stok[pos] = t;
     }
 }
 
-// One wave per window of EMB_WIN sorted rows; each lane owns 4 columns per pass.
+// One wave per (window of EMB_WIN sorted rows, chunk of 256 columns); each lane
+// owns 4 columns.
 __global__ __launch_bounds__(256) void emb_segsum_kernel(const int32_t* __restrict__ order,
                                                          const int32_t* __restrict__ stok,
-                                                         const int32_t* __restrict__ start, int V,
+                                                         const int32_t* __restrict__ nvalid,
                                                          const uint16_t* __restrict__ dx, int C,
                                                          float* __restrict__ dwte) {
-    const int n = start[V];
-    const int wv = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * 256 + threadIdx.x) >> 6));
+    const int n = *nvalid;
+    const int nch = (C / 4 + 63) / 64;
+    const int wid = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * 256 + threadIdx.x) >> 6));
+    const int wv = wid / nch, ch = wid % nch;
     const int lane = threadIdx.x & 63;
     const int p0 = wv * EMB_WIN;
     if (p0 >= n) return;
     const int p1 = min(p0 + EMB_WIN, n);
     const bool head_shared = p0 > 0 && stok[p0 - 1] == stok[p0];
     const bool tail_shared = p1 < n && stok[p1] == stok[p1 - 1];
-    for (int c4 = lane; c4 < C / 4; c4 += 64) {
+    {
+        const int c4 = ch * 64 + lane;
+        if (c4 >= C / 4) return;
         u32x2 gv[EMB_WIN];
 #pragma unroll
         for (int q = 0; q < EMB_WIN; ++q)
@@ -507,23 +461,23 @@ hipError_t launch_embedding_bwd(const int32_t* tok, const uint16_t* dx, float* d
     const int64_t rows = (int64_t)B * T;
     if (C % 4 || V > 65536 || work == nullptr || work_elems < embedding_bwd_work_elems(rows, V) || rows > INT32_MAX)
         return hipErrorInvalidValue;
-    int32_t* counts = work;
-    int32_t* start = counts + V;
-    int32_t* cursor = start + V + 1;
-    int32_t* order = cursor + V;
-    int32_t* stok = order + rows;
-    const int rb = (int)cdiv(rows, 256);
-    const int nwin = (int)cdiv(rows, EMB_WIN);
-    PROF_LAUNCH(KC_EMB_BWD_WTE, 4.0 * rows * C + 8.0 * rows * C, s, {
-        hipLaunchKernelGGL(emb_zero_kernel, dim3(cdiv(V, 256)), dim3(256), 0, s, counts, V);
-        hipLaunchKernelGGL(emb_count_kernel, dim3(rb), dim3(256), 0, s, tok, rows, V, counts);
-        hipLaunchKernelGGL(emb_scan_kernel, dim3(1), dim3(1024), 0, s, counts, V, start, cursor);
-        hipLaunchKernelGGL(emb_scatter_kernel, dim3(rb), dim3(256), 0, s, tok, rows, V, cursor, order, stok);
-        hipLaunchKernelGGL(emb_segsum_kernel, dim3(cdiv(nwin, 4)), dim3(256), 0, s, order, stok, start, V, dx, C,
-                           dwte);
-    });
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // the sort keeps 16-bit offsets: batches of more rows go in chunks
+    constexpr int64_t CHUNK = 65535;
+    int32_t* nvalid = work;
+    int32_t* order = work + 1;
+    int32_t* stok = order + std::min(rows, CHUNK);
+    for (int64_t r0 = 0; r0 < rows; r0 += CHUNK) {
+        const int64_t n = std::min(CHUNK, rows - r0);
+        const int64_t nwaves = cdiv(n, EMB_WIN) * cdiv(C / 4, 64);
+        PROF_LAUNCH(KC_EMB_BWD_WTE, 4.0 * n * C + 8.0 * n * C, s, {
+            hipLaunchKernelGGL(emb_sort_kernel, dim3(1), dim3(EMB_SORT_THREADS), 0, s, tok + r0, (int)n, V, order,
+                               stok, nvalid);
+            hipLaunchKernelGGL(emb_segsum_kernel, dim3((unsigned)cdiv(nwaves, 4)), dim3(256), 0, s, order, stok,
+                               nvalid, dx + r0 * C, C, dwte);
+        });
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     PROF_LAUNCH(KC_EMB_BWD_WPE, 2.0 * rows * C + 8.0 * T * C, s, hipLaunchKernelGGL(embedding_bwd_wpe_kernel, dim3(grid_for((int64_t)T * C)), dim3(256), 0, s, dx, dwpe, B, T, C));
     return hipGetLastError();
 }
