@@ -89,9 +89,11 @@ struct Stage {
 
 // ---------------------------------------------------------------- forward
 
-// Each workgroup iteration: the wave's 8 K fragments are read, the 8 S^T MFMAs
-// issued, the 8 V^T fragments for this block read (their latency hidden by the
-// softmax), then the 8 O^T MFMAs.  Scores stay in raw units: the max is taken
+// Each workgroup iteration: per 32-key half the wave reads its 4 K fragments
+// and issues the S^T MFMAs; after the softmax it reads the V^T fragments one
+// 16-key step at a time, just ahead of that step's O^T MFMAs.  Holding no
+// more fragments than that keeps the kernel at 128 VGPRs (four waves per
+// SIMD), and the other waves cover the LDS latency.  Scores stay in raw units: the max is taken
 // on raw scores and exp2(s * scale*log2e - m * scale*log2e) is one FMA + exp.
 // Masks are applied only on blocks that straddle the diagonal; the reference
 // max (and with it O and l) is moved only when a block max exceeds it by more
@@ -145,26 +147,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
             stv.load(Vg, ld, s0 + KVB, tid);
         }
         if (qw < T && s0 <= q_last_w) {
-            bf16x8 kfr[2][KK], vfr[KVB / 16][DT];
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) kfr[st][kk] = frag_rows(sK[buf], LD, st * 32, kk, lane);
-            __builtin_amdgcn_sched_barrier(0);
             floatx16 sacc[2];
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
+                bf16x8 kfr[KK];
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) kfr[kk] = frag_rows(sK[buf], LD, st * 32, kk, lane);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sacc[st][r] = 0.f;
 #pragma unroll
-                for (int kk = 0; kk < KK; ++kk) sacc[st] = mfma32(kfr[st][kk], qf[kk], sacc[st]);
+                for (int kk = 0; kk < KK; ++kk) sacc[st] = mfma32(kfr[kk], qf[kk], sacc[st]);
             }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int ks = 0; ks < KVB / 16; ++ks)
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) vfr[ks][dt] = frag_tr(sV[buf], LD, ks, dt * 32, lane);
-            __builtin_amdgcn_sched_barrier(0);
             if (s0 + KVB - 1 > qw) {  // block straddles the diagonal for this wave
 #pragma unroll
                 for (int st = 0; st < 2; ++st)
@@ -210,9 +203,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
             }
             l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 #pragma unroll
-            for (int ks = 0; ks < KVB / 16; ++ks)
+            for (int ks = 0; ks < KVB / 16; ++ks) {
+                bf16x8 vfr[DT];
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(vfr[ks][dt], pf[ks], acc[dt]);
+                for (int dt = 0; dt < DT; ++dt) vfr[dt] = frag_tr(sV[buf], LD, ks, dt * 32, lane);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(vfr[dt], pf[ks], acc[dt]);
+            }
         }
         if (kb + 1 < nkv) {
             // buffer buf^1 was last read in step kb-1, before the previous barrier
