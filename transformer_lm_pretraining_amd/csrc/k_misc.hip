@@ -132,7 +132,8 @@ __global__ __launch_bounds__(XE_THREADS) void xent_kernel(uint16_t* __restrict__
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int vid = tid + XE_THREADS * i;
-        v[i] = vid < nvec ? z[vid] : u32x4{0, 0, 0, 0};
+        // the row is read once and its gradient written once: non-temporal hints
+        v[i] = vid < nvec ? __builtin_nontemporal_load(z + vid) : u32x4{0, 0, 0, 0};
     }
     auto elem = [&](int i, int e) { return (e & 1) ? bfhi(v[i][e >> 1]) : bflo(v[i][e >> 1]); };
     // pass 1: row max over the real columns
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(XE_THREADS) void xent_kernel(uint16_t* __restrict__
             for (int e = 0; e < 8; ++e)
                 if (e == (t & 7)) d[e] -= dloss;
         }
-        z[vid] = u32x4{pack_bf2(d[0], d[1]), pack_bf2(d[2], d[3]), pack_bf2(d[4], d[5]), pack_bf2(d[6], d[7])};
+        __builtin_nontemporal_store(u32x4{pack_bf2(d[0], d[1]), pack_bf2(d[2], d[3]), pack_bf2(d[4], d[5]), pack_bf2(d[6], d[7])}, z + vid);
     }
 }
 

@@ -64,6 +64,15 @@ __device__ __forceinline__ float adam_one(float& p, float g, float& m, float& v,
     return p;
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_nt(const float4* p) {
+    const f32x4 v = __builtin_nontemporal_load((const f32x4*)p);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt(float4* p, float4 v) {
+    __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, (f32x4*)p);
+}
+
 __global__ __launch_bounds__(OPT_THREADS) void adamw_kernel(float4* __restrict__ p, float4* __restrict__ g,
                                                             float4* __restrict__ m, float4* __restrict__ v,
                                                             uint2* __restrict__ shadow, int64_t n4,
@@ -71,17 +80,19 @@ __global__ __launch_bounds__(OPT_THREADS) void adamw_kernel(float4* __restrict__
                                                             const float* __restrict__ scale_ptr) {
     const float sc = scale_ptr[0];
     for (int64_t i = blockIdx.x * (int64_t)OPT_THREADS + threadIdx.x; i < n4; i += (int64_t)gridDim.x * OPT_THREADS) {
-        float4 pp = p[i], gg = g[i], mm = m[i], vv = v[i];
+        // streaming: each element is touched once per step, so the loads and
+        // stores carry the non-temporal hint
+        float4 pp = ld_nt(p + i), gg = ld_nt(g + i), mm = ld_nt(m + i), vv = ld_nt(v + i);
         const bool dec = i < n_decay4;
         const float wd = dec ? a.wd : 0.0f;
         adam_one(pp.x, gg.x * sc, mm.x, vv.x, wd, a);
         adam_one(pp.y, gg.y * sc, mm.y, vv.y, wd, a);
         adam_one(pp.z, gg.z * sc, mm.z, vv.z, wd, a);
         adam_one(pp.w, gg.w * sc, mm.w, vv.w, wd, a);
-        p[i] = pp;
-        m[i] = mm;
-        v[i] = vv;
-        g[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        st_nt(p + i, pp);
+        st_nt(m + i, mm);
+        st_nt(v + i, vv);
+        st_nt(g + i, make_float4(0.f, 0.f, 0.f, 0.f));
         if (dec && shadow) shadow[i] = make_uint2(pack_bf2(pp.x, pp.y), pack_bf2(pp.z, pp.w));
     }
 }
