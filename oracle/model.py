@@ -171,7 +171,9 @@ def forward(cfg: Config, P, tok, tgt=None, dtype=np.float64):
         return None, None, cache
     loss_rows, probs = ops.masked_xent_fwd(z.reshape(B * T, -1), tgt.reshape(-1), cfg.V)
     cache["probs"] = probs
-    return float(loss_rows.mean()), loss_rows.reshape(B, T), cache
+    n_keep = int(np.count_nonzero(tgt != ops.IGNORE_TARGET))
+    mean = float(loss_rows.sum() / n_keep) if n_keep else 0.0  # mean over the positions whose loss is taken
+    return mean, loss_rows.reshape(B, T), cache
 
 
 def backward(cfg: Config, P, cache, dloss, dtype=np.float64):
@@ -219,8 +221,9 @@ def backward(cfg: Config, P, cache, dloss, dtype=np.float64):
 
 
 def loss_and_grads(cfg: Config, P, tok, tgt, dloss=None, dtype=np.float64):
-    """Mean loss and gradients of dloss * sum of row losses (default dloss = 1/(B*T): the mean)."""
+    """Mean loss and gradients of dloss * sum of row losses (default dloss = 1 / the number of
+    positions whose target is not ignored: the gradient of the mean)."""
     if dloss is None:
-        dloss = 1.0 / tok.size
+        dloss = 1.0 / max(1, int(np.count_nonzero(tgt != ops.IGNORE_TARGET)))
     loss, rows, cache = forward(cfg, P, tok, tgt, dtype=dtype)
     return loss, backward(cfg, P, cache, dloss, dtype=dtype), cache

@@ -112,24 +112,36 @@ def attention_bwd(do, q, k, v, p):
 # around Fig. 1: the softmax covers only the V real tokens, so the padding
 # columns get no probability and no gradient).
 
+# A target of IGNORE_TARGET marks a position whose loss is not taken (PDS,
+# clinical-adaptation paragraph: the loss is taken on answers, not on
+# questions): its row loss is 0 and its gradient row is 0.
+IGNORE_TARGET = -100
+
+
 def masked_xent_fwd(z, tgt, V):
-    """z: [R, Vp] logits, tgt: [R] ids < V.  Returns per-row loss [R] and probs [R, V]."""
+    """z: [R, Vp] logits, tgt: [R] ids < V or IGNORE_TARGET.  Returns per-row loss [R]
+    (0 on ignored rows) and probs [R, V]."""
     zr = z[:, :V]
     mx = zr.max(axis=1, keepdims=True)
     e = np.exp(zr - mx)
     den = e.sum(axis=1, keepdims=True)
     lse = mx[:, 0] + np.log(den[:, 0])
-    loss = lse - zr[np.arange(z.shape[0]), tgt]
+    keep = tgt != IGNORE_TARGET
+    t = np.where(keep, tgt, 0)
+    loss = np.where(keep, lse - zr[np.arange(z.shape[0]), t], 0.0)
     return loss, e / den
 
 
 def masked_xent_bwd(probs, tgt, Vp, dloss):
-    """d(dloss * sum_r loss_r)/dz: (p - onehot) * dloss on real columns, exactly 0 on padding."""
+    """d(dloss * sum_r loss_r)/dz: (p - onehot) * dloss on real columns, exactly 0 on padding
+    and on the rows of ignored targets."""
     R, V = probs.shape
+    keep = tgt != IGNORE_TARGET
     dz = np.zeros((R, Vp), dtype=probs.dtype)
     dz[:, :V] = probs
-    dz[np.arange(R), tgt] -= 1.0
+    dz[np.arange(R)[keep], tgt[keep]] -= 1.0
     dz[:, :V] *= dloss
+    dz[~keep] = 0.0
     return dz
 
 

@@ -254,6 +254,61 @@ def test_masked_xent_matches_log_softmax_and_ignores_padding():
     np.testing.assert_allclose(loss2, loss, rtol=1e-12)
 
 
+def test_masked_xent_ignored_targets():
+    """Ignored positions (answer-only loss in the PDS clinical-adaptation paragraph): loss 0
+    and gradient 0 on their rows; the other rows equal scipy's log-softmax and softmax."""
+    rs = np.random.default_rng(16)
+    V, Vp, R = 61, 64, 9
+    z = rs.standard_normal((R, Vp))
+    z[:, V:] = 1e3
+    tgt = rs.integers(0, V, R)
+    tgt[[1, 4, 5]] = ops.IGNORE_TARGET
+    keep = tgt != ops.IGNORE_TARGET
+    loss, probs = ops.masked_xent_fwd(z, tgt, V)
+    ls = special.log_softmax(z[:, :V], axis=1)
+    assert np.all(loss[~keep] == 0)
+    np.testing.assert_allclose(loss[keep], -ls[keep, tgt[keep]], rtol=1e-13)
+    dz = ops.masked_xent_bwd(probs, tgt, Vp, 0.5)
+    assert np.all(dz[~keep] == 0) and np.all(dz[:, V:] == 0)
+    want = np.exp(ls[keep])
+    want[np.arange(keep.sum()), tgt[keep]] -= 1.0
+    np.testing.assert_allclose(dz[keep, :V], 0.5 * want, rtol=1e-12, atol=1e-15)
+
+
+def test_masked_loss_model_mean_and_finite_differences():
+    """Model level: the loss with ignored targets is the mean of the unmasked row losses over
+    the kept positions, and its gradient matches central differences."""
+    cfg = CONFIGS["micro"]
+    P = {k: v.astype(np.float64) for k, v in init_params(cfg, 9).items()}
+    rs = np.random.default_rng(17)
+    for k in P:
+        if k.endswith("bias") or k.startswith("ln_f") or ".ln_" in k:
+            P[k] = P[k] + 0.1 * rs.standard_normal(P[k].shape)
+    P["wte"][cfg.V:] = 0.0
+    tok = rs.integers(0, cfg.V, (2, 8))
+    tgt = rs.integers(0, cfg.V, (2, 8))
+    full_rows = forward(cfg, P, tok, tgt, dtype=np.float64)[1]
+    tgt_m = tgt.copy()
+    tgt_m[0, :5] = ops.IGNORE_TARGET  # a "question" prefix
+    tgt_m[1, 2] = ops.IGNORE_TARGET
+    keep = tgt_m != ops.IGNORE_TARGET
+    loss, G, _ = loss_and_grads(cfg, P, tok, tgt_m, dtype=np.float64)
+    assert loss == pytest.approx(full_rows[keep].mean(), rel=1e-12)
+
+    def f(PP):
+        return forward(cfg, PP, tok, tgt_m, dtype=np.float64)[0]
+
+    for name in ("wte", "h.0.attn.c_attn.weight", "h.1.mlp.c_fc.bias", "ln_f.weight"):
+        g = G[name]
+        for fi in rs.choice(g.size, size=6, replace=False):
+            idx = np.unravel_index(fi, g.shape)
+            base = P[name][idx]
+            h = 1e-6 * max(1.0, abs(base))
+            Pp = dict(P); Pp[name] = P[name].copy(); Pp[name][idx] = base + h
+            Pm = dict(P); Pm[name] = P[name].copy(); Pm[name][idx] = base - h
+            assert (f(Pp) - f(Pm)) / (2 * h) == pytest.approx(g[idx], rel=1e-5, abs=1e-9), (name, idx)
+
+
 def test_embedding_backward_collisions():
     tok = np.array([[3, 3, 1], [3, 0, 1]])
     dx = np.arange(2 * 3 * 2, dtype=np.float64).reshape(2, 3, 2)
