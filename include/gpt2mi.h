@@ -149,15 +149,24 @@ int gpt2_init(const gpt2_config* cfg, uint64_t seed, const float* host_init, con
               hipStream_t stream, gpt2_handle** out);
 
 /*
+ * Target id of a position whose loss is not taken (answer-only loss in the
+ * PDS clinical-adaptation paragraph): its row loss and logit gradient are 0,
+ * and it is left out of the mean loss.
+ */
+#define GPT2_IGNORE_TARGET (-100)
+
+/*
  * Forward pass on device-resident ids tok, tgt (int32 [B, T], row-major).
  * Saves the activations needed by gpt2_backward.  With tgt != NULL it runs
  * the masked softmax cross-entropy over the V real columns (PDS model text:
  * padding columns get no probability), leaves the bf16 logit gradient
  * (softmax - onehot) * dloss_scale in the logits buffer for gpt2_backward
- * (exactly 0 on the padding columns), and writes the mean loss over the B*T
- * rows to loss_dev[0] (fp32, device) if loss_dev != NULL.  dloss_scale is
- * the weight of one row's loss in the optimised objective: 1/(B*T*n_micro)
- * for the mean over an accumulated step.  With tgt == NULL only the bf16
+ * (exactly 0 on the padding columns), and writes the mean loss over the rows
+ * whose target is not GPT2_IGNORE_TARGET (0 if there are none) to loss_dev[0]
+ * (fp32, device) if loss_dev != NULL.  Ignored rows get loss 0 and a zero
+ * logit gradient.  dloss_scale is the weight of one row's loss in the
+ * optimised objective: 1/(kept rows over the n_micro micro-steps) for the
+ * mean over an accumulated step (1/(B*T*n_micro) when nothing is ignored).  With tgt == NULL only the bf16
  * logits [B*T, Vp] are produced (read them with gpt2_logits_ptr).
  * Errors: GPT2_E_INVALID (null tok), GPT2_E_HIP.
  */
@@ -187,8 +196,8 @@ int gpt2_clip_adamw(gpt2_handle* h, const gpt2_adamw_args* args, float* grad_nor
 
 /*
  * Held-out loss: forward + masked cross-entropy (no gradient written),
- * synchronises the stream and returns the mean loss over the B*T rows in
- * *loss_host.  Errors: GPT2_E_INVALID, GPT2_E_DATA (bad ids seen since the
+ * synchronises the stream and returns the mean loss over the rows whose
+ * target is not GPT2_IGNORE_TARGET in *loss_host.  Errors: GPT2_E_INVALID, GPT2_E_DATA (bad ids seen since the
  * last status read), GPT2_E_HIP.
  */
 int gpt2_eval_loss(gpt2_handle* h, const int32_t* tok, const int32_t* tgt, float* loss_host, hipStream_t stream);

@@ -24,8 +24,9 @@ extern "C" {
  * tokens; padding columns get no probability and no gradient).  logits: bf16
  * [rows, Vp], overwritten in place when write_grad != 0 by
  * (softmax_j - [j == tgt]) * dloss for j < V and exactly 0 for j >= V.
- * loss_rows: fp32 [rows] = logsumexp_{j<V} z - z_tgt.  Ids outside [0, V)
- * set *flag (int32, device, may be NULL) to 1 and are clamped.
+ * loss_rows: fp32 [rows] = logsumexp_{j<V} z - z_tgt.  A target equal to
+ * GPT2_IGNORE_TARGET gives loss 0 and an all-zero gradient row; other ids
+ * outside [0, V) set *flag (int32, device, may be NULL) to 1 and are clamped.
  * Requires Vp % 128 == 0, 1 <= V <= Vp, Vp <= 65536.
  */
 int gpt2k_xent(uint16_t* logits, const int32_t* tgt, float* loss_rows, int64_t rows, int32_t V, int32_t Vp,

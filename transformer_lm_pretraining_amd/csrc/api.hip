@@ -334,14 +334,14 @@ int run_forward(gpt2_handle* h, const int32_t* tok, const int32_t* tgt, float dl
         HIPCHK(launch_xent(h->act<uint16_t>(h->acts.logits), tgt, h->act<float>(h->acts.loss_rows), BT, c.V, c.Vp,
                            dloss, train ? 1 : 0, flag, s));
         float* ldst = loss_dev ? loss_dev : (float*)(h->S() + h->scr.loss);
-        HIPCHK(launch_mean(h->act<float>(h->acts.loss_rows), BT, ldst, s));
+        HIPCHK(launch_mean(h->act<float>(h->acts.loss_rows), tgt, BT, ldst, s));
     }
     return GPT2_OK;
 }
 
-// The four weight-gradient products of block l, one grouped launch (run once
-// the block's input gradient is done, so their dY tensors are all still held:
-// the residual-stream gradients at the block output and at x_mid, dpre, dqkv).
+// Weight-gradient product `which` of block l (its dY tensors: the residual-stream
+// gradients at the block output and at x_mid, dpre, dqkv, all kept until the
+// products of every block run together after the last block).
 TnJobDesc block_dw_job(gpt2_handle* h, int l, int which, const uint16_t* d_out, const uint16_t* d_mid,
                        const uint16_t* d_pre, const uint16_t* d_qkv) {
     const gpt2_config& c = h->cfg;

@@ -128,6 +128,13 @@ __global__ __launch_bounds__(XE_THREADS) void xent_kernel(uint16_t* __restrict__
     u32x4* z = (u32x4*)(logits + row * (int64_t)Vp);
     const int nvec = Vp / 8, nfull = V / 8;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int t = tgt[row];
+    if (t == GPT2_IGNORE_TARGET) {  // loss not taken here: zero loss, zero gradient row
+        if (tid == 0) loss_rows[row] = 0.f;
+        if (write_grad)
+            for (int vid = tid; vid < nvec; vid += XE_THREADS) z[vid] = u32x4{0u, 0u, 0u, 0u};
+        return;
+    }
     u32x4 v[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -178,7 +185,6 @@ __global__ __launch_bounds__(XE_THREADS) void xent_kernel(uint16_t* __restrict__
     sum = 0.f;
 #pragma unroll
     for (int w = 0; w < XE_THREADS / 64; ++w) sum += red[w];
-    int t = tgt[row];
     if (t < 0 || t >= V) {
         if (tid == 0 && flag) atomicOr(flag, 1);
         t = t < 0 ? 0 : V - 1;
@@ -210,17 +216,30 @@ __global__ __launch_bounds__(XE_THREADS) void xent_kernel(uint16_t* __restrict__
     }
 }
 
-__global__ __launch_bounds__(1024) void mean_kernel(const float* __restrict__ x, int64_t n, float* __restrict__ out) {
+__global__ __launch_bounds__(1024) void mean_kernel(const float* __restrict__ x, const int32_t* __restrict__ tgt,
+                                                     int64_t n, float* __restrict__ out) {
     __shared__ double red[16];
-    double s = 0.0;
-    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) s += x[i];
+    __shared__ double cnt[16];
+    double s = 0.0, c = 0.0;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+        if (tgt && tgt[i] == GPT2_IGNORE_TARGET) continue;
+        s += x[i];
+        c += 1.0;
+    }
     s = wave_sum_d(s);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+    c = wave_sum_d(c);
+    if ((threadIdx.x & 63) == 0) {
+        red[threadIdx.x >> 6] = s;
+        cnt[threadIdx.x >> 6] = c;
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
-        double t = 0.0;
-        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
-        out[0] = (float)(t / (double)n);
+        double t = 0.0, k = 0.0;
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+            t += red[w];
+            k += cnt[w];
+        }
+        out[0] = k > 0.0 ? (float)(t / k) : 0.0f;
     }
 }
 
@@ -442,8 +461,8 @@ hipError_t launch_xent(uint16_t* logits, const int32_t* tgt, float* loss_rows, i
     return hipGetLastError();
 }
 
-hipError_t launch_mean(const float* x, int64_t n, float* out, hipStream_t s) {
-    PROF_LAUNCH(KC_MEAN, 4.0 * n, s, hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(1024), 0, s, x, n, out));
+hipError_t launch_mean(const float* x, const int32_t* tgt, int64_t n, float* out, hipStream_t s) {
+    PROF_LAUNCH(KC_MEAN, 8.0 * n, s, hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(1024), 0, s, x, tgt, n, out));
     return hipGetLastError();
 }
 

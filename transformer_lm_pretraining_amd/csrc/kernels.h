@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gpt2mi.h"  // GPT2_IGNORE_TARGET
+
 // ---- GEMM (k_gemm.hip) -----------------------------------------------------
 // out[M,N] = A[M,K] . B[N,K]^T (+bias[N]) (+res[M,N]); K % 64 == 0.
 hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M, int N, int K,
@@ -65,7 +67,8 @@ hipError_t launch_bias_grad(const uint16_t* dY, int64_t ldy, float* db, float* p
                             hipStream_t s);
 hipError_t launch_xent(uint16_t* logits, const int32_t* tgt, float* loss_rows, int64_t rows, int V, int Vp,
                        float dloss, int write_grad, int32_t* flag, hipStream_t s);
-hipError_t launch_mean(const float* x, int64_t n, float* out, hipStream_t s);
+// out[0] = mean of x over the rows whose target is not GPT2_IGNORE_TARGET (tgt may be null: all rows).
+hipError_t launch_mean(const float* x, const int32_t* tgt, int64_t n, float* out, hipStream_t s);
 hipError_t launch_embedding_fwd(const int32_t* tok, const uint16_t* wte, const uint16_t* wpe, uint16_t* x, int B,
                                 int T, int C, int V, int32_t* flag, hipStream_t s);
 // work: embedding_bwd_work_elems(B*T, V) int32 scratch (counting sort of the rows by token)

@@ -17,6 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgpt2mi.so")
 
 GPT2_OK, GPT2_E_INVALID, GPT2_E_SHAPE, GPT2_E_STATE, GPT2_E_HIP, GPT2_E_DATA, GPT2_E_UNSUPPORTED = range(7)
+IGNORE_TARGET = -100  # GPT2_IGNORE_TARGET: a position whose loss is not taken
 # kernel classes whose work is counted in FLOP (the others count bytes)
 MFMA_CLASSES = ("gemm_nt", "gemm_nt_gelu", "gemm_tn_acc", "gemm_tn_splitk", "attn_fwd", "attn_dkdv", "attn_dq")
 
