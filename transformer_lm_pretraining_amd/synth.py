@@ -84,3 +84,57 @@ def normal(shape, std: float = 1.0, seed: int = DEFAULT_SEED, stream: int = STRE
 def targets(rows: int, V: int, seed: int = DEFAULT_SEED) -> np.ndarray:
     """Targets for kernel-level loss inputs: the first `rows` ids of the token stream shifted by one."""
     return token_stream(rows + 1, V, seed)[1:].astype(np.int32)
+
+
+class TokenStream:
+    """Resumable stream of the same Zipf/EOT law as token_stream (a different draw
+    order, so not the same ids for a seed).  Documents are drawn 64 at a time;
+    state() captures the generator state and the unread tokens, and
+    TokenStream.from_state() continues exactly where state() was taken."""
+
+    DOCS_PER_DRAW = 64
+
+    def __init__(self, V: int, seed: int = DEFAULT_SEED, stream: int = STREAM_TOKENS):
+        self.V = V
+        self.rng = child_rng(seed, stream)
+        self.cdf = zipf_cdf(V - 1)
+        self.buf = np.empty(0, dtype=np.int32)
+
+    def _draw(self):
+        V, n = self.V, self.DOCS_PER_DRAW
+        lens = self.rng.geometric(DOC_P, size=n).astype(np.int64)
+        body = np.searchsorted(self.cdf, self.rng.random(int(lens.sum())), side="right").astype(np.int32)
+        np.minimum(body, V - 2, out=body)
+        chunk = np.empty(int(lens.sum()) + n, dtype=np.int32)
+        starts = np.concatenate(([0], np.cumsum(lens + 1)[:-1]))
+        is_eot = np.zeros(chunk.size, dtype=bool)
+        is_eot[starts] = True
+        chunk[is_eot] = V - 1
+        chunk[~is_eot] = body
+        self.buf = np.concatenate((self.buf, chunk))
+
+    def take(self, n: int, keep_last: bool = False) -> np.ndarray:
+        """The next n ids; with keep_last the n-th id is also the first of the next take."""
+        while self.buf.size < n:
+            self._draw()
+        out = self.buf[:n].copy()
+        self.buf = self.buf[n - 1 if keep_last else n:]
+        return out
+
+    def state(self) -> dict:
+        return {"V": self.V, "rng": self.rng.bit_generator.state, "buf": self.buf.tolist()}
+
+    @classmethod
+    def from_state(cls, st: dict) -> "TokenStream":
+        obj = cls.__new__(cls)
+        obj.V = int(st["V"])
+        obj.rng = np.random.default_rng()
+        obj.rng.bit_generator.state = st["rng"]
+        obj.cdf = zipf_cdf(obj.V - 1)
+        obj.buf = np.asarray(st["buf"], dtype=np.int32)
+        return obj
+
+    def micro_batch(self, B: int, T: int):
+        """(tok, tgt) int32 [B, T] from the next B*T+1 ids (consecutive micro-batches share one id)."""
+        chunk = self.take(B * T + 1, keep_last=True)
+        return chunk[:-1].reshape(B, T).copy(), chunk[1:].reshape(B, T).copy()

@@ -1,0 +1,238 @@
+"""Training loop around the C ABI, after Pretraining and adapting a language model
+on a dependency-free stack:
+
+* an optimizer step is n_micro forward/backward micro-steps accumulated into the
+  fp32 gradients, then global-norm clip + AdamW (§4.4 batch, §4 optimisation);
+* the learning rate rises linearly over 700 steps to 6e-4, then follows a
+  cosine to 0 at step 18,865 (§4 optimisation);
+* held-out cross-entropy is the mean over 180 fixed batches, every 250 steps
+  (evaluation paragraph);
+* checkpoints every 500 steps hold the parameters, the AdamW moments, the step
+  and the data cursor, so a restart resumes rather than repeats; a supervisor
+  relaunches a crashed run from its latest checkpoint and stops for good on a
+  completion or a halt marker (supervision paragraph).
+
+Data are synthetic (synth.TokenStream: a Zipf/end-of-text stream standing in
+for the FineWeb shards).  Every GPU operation is a call into libgpt2mi.so.
+
+    python -m transformer_lm_pretraining_amd.train --run-dir runs/a --steps 1000
+    python -m transformer_lm_pretraining_amd.train --run-dir runs/a --steps 1000 --supervise
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import shutil
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+from . import lib, synth
+
+MAX_LR = 6e-4
+WARMUP_STEPS = 700
+TOTAL_STEPS = 18865
+EVAL_EVERY = 250
+EVAL_BATCHES = 180
+CKPT_EVERY = 500
+COMPLETE_MARKER = "COMPLETE"
+HALT_MARKER = "HALT"
+
+WORKLOADS = {
+    # name: (L, H, C, V, Vp, Tmax, B, T, n_micro)
+    "gpt2_124m": (12, 12, 768, 50257, 50304, 1024, 19, 1024, 9),
+    "tiny": (2, 4, 128, 50257, 50304, 64, 4, 64, 2),
+}
+
+
+def lr_at(step: int, max_lr: float = MAX_LR, warmup: int = WARMUP_STEPS, total: int = TOTAL_STEPS) -> float:
+    """Learning rate of 1-based optimizer step `step`: step/warmup * max_lr during the
+    warmup, then 0.5 max_lr (1 + cos(pi (step - warmup) / (total - warmup)))."""
+    if step <= warmup:
+        return max_lr * step / warmup
+    frac = min(1.0, (step - warmup) / (total - warmup))
+    return 0.5 * max_lr * (1.0 + math.cos(math.pi * frac))
+
+
+class Trainer:
+    """One model, its training stream and its fixed held-out batches."""
+
+    def __init__(self, workload: str = "gpt2_124m", seed: int = 1337, data_seed: int = 1,
+                 eval_seed: int = 2, device: str = "cuda", init=None):
+        """init: optional host fp32 flat parameters in place of the seeded initialisation."""
+        import torch
+        L, H, C, V, Vp, Tmax, B, T, n_micro = WORKLOADS[workload]
+        self.workload, self.seed, self.eval_seed = workload, seed, eval_seed
+        self.B, self.T, self.V, self.n_micro = B, T, V, n_micro
+        self.cfg = lib.make_config(L, H, C, V, Vp, Tmax, B, T)
+        self.model = lib.GPT2(self.cfg, seed=seed, init=init, device=device)
+        self.data = synth.TokenStream(V, data_seed)
+        self.step = 0  # completed optimizer steps
+        self.device = torch.device(device)
+        self._eval = None
+
+    def _dev(self, a):
+        import torch
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(self.device)
+
+    def train_step(self):
+        """One optimizer step; returns (mean training loss, gradient norm before clipping, lr)."""
+        import torch
+        m = self.model
+        losses = torch.zeros(self.n_micro, dtype=torch.float32, device=self.device)
+        dloss = 1.0 / (self.B * self.T * self.n_micro)
+        for k in range(self.n_micro):
+            tok, tgt = self.data.micro_batch(self.B, self.T)
+            m.forward(self._dev(tok), self._dev(tgt), dloss=dloss, loss_out=losses[k:k + 1])
+            m.backward()
+        lr = lr_at(self.step + 1)
+        norm = m.clip_adamw(lr, self.step + 1)
+        self.step += 1
+        return float(losses.mean().item()), float(norm.item()), lr
+
+    def held_out_batches(self, n: int):
+        """The same n held-out micro-batches at every evaluation (a stream of their own)."""
+        if self._eval is None or len(self._eval) < n:
+            s = synth.TokenStream(self.V, self.eval_seed)
+            self._eval = [tuple(self._dev(a) for a in s.micro_batch(self.B, self.T)) for _ in range(n)]
+        return self._eval[:n]
+
+    def evaluate(self, n_batches: int = EVAL_BATCHES) -> float:
+        """Mean held-out cross-entropy over n_batches micro-batches (gpt2_eval_loss each)."""
+        losses = [self.model.eval_loss(tok, tgt) for tok, tgt in self.held_out_batches(n_batches)]
+        return float(np.mean(losses))
+
+    # ---- checkpoints
+    def save(self, run_dir: str) -> str:
+        """Writes run_dir/step_XXXXXXX (params, m, v as fp32 .npy; step, workload, seeds and the
+        data cursor as JSON) via a temporary directory, then points run_dir/latest at it."""
+        name = f"step_{self.step:07d}"
+        final = os.path.join(run_dir, name)
+        tmp = final + ".tmp"
+        shutil.rmtree(tmp, ignore_errors=True)
+        os.makedirs(tmp)
+        m = self.model
+        for key, t in (("params", m.params), ("m", m.m), ("v", m.v)):
+            np.save(os.path.join(tmp, key + ".npy"), t.detach().cpu().numpy())
+        meta = {"step": self.step, "workload": self.workload, "seed": self.seed, "eval_seed": self.eval_seed,
+                "data": self.data.state()}
+        with open(os.path.join(tmp, "meta.json"), "w") as f:
+            json.dump(meta, f)
+        shutil.rmtree(final, ignore_errors=True)
+        os.replace(tmp, final)
+        latest_tmp = os.path.join(run_dir, "latest.tmp")
+        with open(latest_tmp, "w") as f:
+            f.write(name)
+        os.replace(latest_tmp, os.path.join(run_dir, "latest"))
+        return final
+
+    @classmethod
+    def resume(cls, run_dir: str, device: str = "cuda") -> "Trainer":
+        """A trainer continuing from run_dir/latest: parameters, moments, step and data cursor."""
+        import torch
+        with open(os.path.join(run_dir, "latest")) as f:
+            ck = os.path.join(run_dir, f.read().strip())
+        with open(os.path.join(ck, "meta.json")) as f:
+            meta = json.load(f)
+        tr = cls.__new__(cls)
+        L, H, C, V, Vp, Tmax, B, T, n_micro = WORKLOADS[meta["workload"]]
+        tr.workload, tr.seed, tr.eval_seed = meta["workload"], meta["seed"], meta["eval_seed"]
+        tr.B, tr.T, tr.V, tr.n_micro = B, T, V, n_micro
+        tr.cfg = lib.make_config(L, H, C, V, Vp, Tmax, B, T)
+        params = np.load(os.path.join(ck, "params.npy"))
+        tr.model = lib.GPT2(tr.cfg, seed=meta["seed"], init=params, device=device)  # shadows from params
+        for key, t in (("m", tr.model.m), ("v", tr.model.v)):
+            t.copy_(torch.from_numpy(np.load(os.path.join(ck, key + ".npy"))).to(t.device))
+        tr.data = synth.TokenStream.from_state(meta["data"])
+        tr.step = int(meta["step"])
+        tr.device = torch.device(device)
+        tr._eval = None
+        return tr
+
+    def run(self, run_dir: str, total_steps: int, eval_every: int = EVAL_EVERY, eval_batches: int = EVAL_BATCHES,
+            ckpt_every: int = CKPT_EVERY, log=print, fail_at_step: int = 0):
+        """Steps until `total_steps` are done, appending one JSON line per step to
+        run_dir/log.jsonl; stops early on a halt marker; writes the completion marker.
+        fail_at_step > 0 raises after that step (a forced crash, for relaunch tests)."""
+        os.makedirs(run_dir, exist_ok=True)
+        with open(os.path.join(run_dir, "log.jsonl"), "a") as logf:
+            while self.step < total_steps:
+                if os.path.exists(os.path.join(run_dir, HALT_MARKER)):
+                    log(f"halt marker at step {self.step}")
+                    return False
+                t0 = time.perf_counter()
+                loss, norm, lr = self.train_step()
+                dt = time.perf_counter() - t0
+                rec = {"step": self.step, "lr": lr, "loss": loss, "grad_norm": norm,
+                       "tokens_per_s": self.B * self.T * self.n_micro / dt}
+                if eval_every and self.step % eval_every == 0:
+                    rec["eval_loss"] = self.evaluate(eval_batches)
+                logf.write(json.dumps(rec) + "\n")
+                logf.flush()
+                log(json.dumps(rec))
+                if ckpt_every and self.step % ckpt_every == 0:
+                    self.save(run_dir)
+                if fail_at_step and self.step == fail_at_step:
+                    raise RuntimeError(f"forced failure after step {self.step}")
+        with open(os.path.join(run_dir, COMPLETE_MARKER), "w") as f:
+            f.write(str(self.step))
+        return True
+
+
+def supervise(cmd, run_dir: str, max_restarts: int = 10, log=print) -> int:
+    """Runs `cmd` (a list) until it leaves the completion marker in run_dir; relaunches it
+    after a failure (the trainer resumes from run_dir/latest itself); stops for good,
+    without launching, once a halt or completion marker exists.  Returns the number of
+    launches."""
+    launches = 0
+    while True:
+        for marker in (HALT_MARKER, COMPLETE_MARKER):
+            if os.path.exists(os.path.join(run_dir, marker)):
+                log(f"supervisor: {marker} marker present, stopping after {launches} launch(es)")
+                return launches
+        if launches > max_restarts:
+            log(f"supervisor: giving up after {launches} launches")
+            return launches
+        launches += 1
+        rc = subprocess.call(cmd)
+        log(f"supervisor: launch {launches} exited with {rc}")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--run-dir", required=True)
+    ap.add_argument("--steps", type=int, required=True, help="total optimizer steps of the run")
+    ap.add_argument("--workload", default="gpt2_124m", choices=sorted(WORKLOADS))
+    ap.add_argument("--eval-every", type=int, default=EVAL_EVERY)
+    ap.add_argument("--eval-batches", type=int, default=EVAL_BATCHES)
+    ap.add_argument("--ckpt-every", type=int, default=CKPT_EVERY)
+    ap.add_argument("--seed", type=int, default=1337)
+    ap.add_argument("--supervise", action="store_true", help="run the trainer under the relaunching supervisor")
+    ap.add_argument("--max-restarts", type=int, default=10)
+    ap.add_argument("--fail-at-step", type=int, default=0,
+                    help="on a fresh start, crash after this step (relaunch tests)")
+    a = ap.parse_args(argv)
+    if a.supervise:
+        child = [sys.executable, "-m", "transformer_lm_pretraining_amd.train"] + \
+                [x for x in (argv if argv is not None else sys.argv[1:]) if x != "--supervise"]
+        supervise(child, a.run_dir, a.max_restarts)
+        return 0
+    os.makedirs(a.run_dir, exist_ok=True)
+    resumed = os.path.exists(os.path.join(a.run_dir, "latest"))
+    if resumed:
+        tr = Trainer.resume(a.run_dir)
+        print(f"resumed at step {tr.step}", flush=True)
+    else:
+        tr = Trainer(a.workload, seed=a.seed)
+    fail = 0 if resumed else a.fail_at_step
+    ok = tr.run(a.run_dir, a.steps, a.eval_every, a.eval_batches, a.ckpt_every,
+                log=lambda s: print(s, flush=True), fail_at_step=fail)
+    return 0 if ok else 3
+
+
+if __name__ == "__main__":
+    sys.exit(main())
