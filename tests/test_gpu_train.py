@@ -55,6 +55,35 @@ def test_checkpoint_resume_continues_the_run(gpu_lib, tmp_path):
     assert diff <= 2e-5
 
 
+def test_pipelined_run_matches_stepwise(gpu_lib, tmp_path):
+    """run() draws each step's ids while the previous step is on the GPU; its first
+    step's loss is the oracle's on the stream's first micro-batches, and after five
+    steps (with an evaluation and a checkpoint in between) it holds the same
+    parameters as five waited-for steps."""
+    from transformer_lm_pretraining_amd.train import Trainer
+    cfg = CONFIGS["tiny"]
+    say("pipelined run tiny")
+    P = init_params(cfg, 1337)
+    flat = oracle.flatten(cfg, P)
+    a = Trainer("tiny", init=flat)
+    first = a.train_step()[0]
+    for _ in range(4):
+        a.train_step()
+    s = synth.TokenStream(cfg.V, 1)
+    ref = np.mean([forward(cfg, P, *s.micro_batch(a.B, a.T), dtype=np.float64)[0] for _ in range(a.n_micro)])
+    say("step-1 loss", first, "oracle", ref)
+    assert abs(first - ref) <= 2e-2
+    b = Trainer("tiny", init=flat)
+    logs = []
+    assert b.run(str(tmp_path), 5, eval_every=2, eval_batches=2, ckpt_every=3, log=logs.append)
+    recs = [json.loads(x) for x in logs]
+    assert [x["step"] for x in recs if "loss" in x] == [1, 2, 3, 4, 5]
+    assert abs(recs[0]["loss"] - first) <= 1e-4
+    diff = float(np.max(np.abs(a.model.params.cpu().numpy() - b.model.params.cpu().numpy())))
+    say("max |param diff| pipelined vs stepwise:", diff)
+    assert diff <= 2e-5
+
+
 def test_held_out_loss_matches_oracle(gpu_lib):
     from transformer_lm_pretraining_amd.train import Trainer
     cfg = CONFIGS["tiny"]
@@ -81,8 +110,10 @@ def test_supervised_run_survives_a_crash(gpu_lib, tmp_path):
     assert r.returncode == 0
     assert (run / "COMPLETE").read_text() == "6"
     assert (run / "latest").read_text() == "step_0000006"
-    recs = [json.loads(x) for x in (run / "log.jsonl").read_text().splitlines()]
+    lines = [json.loads(x) for x in (run / "log.jsonl").read_text().splitlines()]
+    recs = [x for x in lines if "loss" in x]
     assert [x["step"] for x in recs] == [1, 2, 3, 3, 4, 5, 6]  # step 3 ran, crashed, resumed from step 2
+    assert [x["checkpoint"] for x in lines if "checkpoint" in x] == ["step_0000002", "step_0000004", "step_0000006"]
     assert abs(recs[2]["loss"] - recs[3]["loss"]) <= 1e-4
     assert "eval_loss" in recs[2] and "eval_loss" in recs[6]
     assert abs(recs[2]["eval_loss"] - recs[3]["eval_loss"]) <= 1e-4

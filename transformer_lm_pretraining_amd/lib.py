@@ -205,10 +205,12 @@ class GPT2:
     def backward(self):
         check(self.lib.gpt2_backward(self.h, _stream()), "gpt2_backward")
 
-    def clip_adamw(self, lr, t, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0):
+    def clip_adamw(self, lr, t, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0, norm_out=None):
+        """norm_out: optional fp32 device scalar for the pre-clip norm (default: the model's own)."""
         a = AdamwArgs(lr, beta1, beta2, eps, weight_decay, max_norm, t)
-        check(self.lib.gpt2_clip_adamw(self.h, ctypes.byref(a), _ptr(self.norm_dev), _stream()), "gpt2_clip_adamw")
-        return self.norm_dev
+        out = norm_out if norm_out is not None else self.norm_dev
+        check(self.lib.gpt2_clip_adamw(self.h, ctypes.byref(a), _ptr(out), _stream()), "gpt2_clip_adamw")
+        return out
 
     def eval_loss(self, tok, tgt) -> float:
         out = c_float()

@@ -59,12 +59,17 @@ def lr_at(step: int, max_lr: float = MAX_LR, warmup: int = WARMUP_STEPS, total: 
 
 
 class Trainer:
-    """One model, its training stream and its fixed held-out batches."""
+    """One model, its training stream and its fixed held-out batches.
+
+    The host draws the next optimizer step's micro-batches while the GPU runs the
+    current one: ids go to one of two pinned staging slots and reach the device in
+    one asynchronous copy per step, ordered on the stream behind the previous
+    step's kernels.  Per-step loss and norm land in device slots and are read one
+    step late, so the loop never waits on the GPU except to log."""
 
     def __init__(self, workload: str = "gpt2_124m", seed: int = 1337, data_seed: int = 1,
                  eval_seed: int = 2, device: str = "cuda", init=None):
         """init: optional host fp32 flat parameters in place of the seeded initialisation."""
-        import torch
         L, H, C, V, Vp, Tmax, B, T, n_micro = WORKLOADS[workload]
         self.workload, self.seed, self.eval_seed = workload, seed, eval_seed
         self.B, self.T, self.V, self.n_micro = B, T, V, n_micro
@@ -72,33 +77,88 @@ class Trainer:
         self.model = lib.GPT2(self.cfg, seed=seed, init=init, device=device)
         self.data = synth.TokenStream(V, data_seed)
         self.step = 0  # completed optimizer steps
+        self._setup(device)
+
+    def _setup(self, device):
+        import torch
         self.device = torch.device(device)
+        shape = (self.n_micro, 2, self.B, self.T)
+        self._host = [torch.empty(shape, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self._copied = [None, None]  # event after the last copy out of each staging slot
+        self._batch = torch.empty(shape, dtype=torch.int32, device=self.device)
+        self._loss = torch.zeros((2, self.n_micro), dtype=torch.float32, device=self.device)
+        self._norm = torch.zeros(2, dtype=torch.float32, device=self.device)
+        self._slot = 0
+        self._ready = False  # staging slot self._slot holds the next step's ids
+        self._cursor = None  # stream state before those ids were drawn
+        self._last_end = None
         self._eval = None
 
-    def _dev(self, a):
-        import torch
-        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(self.device)
+    def _fill(self, slot):
+        """Draws the next step's n_micro micro-batches into staging slot `slot`."""
+        if self._copied[slot] is not None:
+            self._copied[slot].synchronize()
+        self._cursor = self.data.state()
+        arr = self._host[slot].numpy()
+        for k in range(self.n_micro):
+            arr[k, 0], arr[k, 1] = self.data.micro_batch(self.B, self.T)
 
-    def train_step(self):
-        """One optimizer step; returns (mean training loss, gradient norm before clipping, lr)."""
+    def launch_step(self):
+        """Queues one optimizer step (n_micro forward/backward micro-steps, then clip +
+        AdamW at lr_at(step + 1)), draws the following step's ids on the host while it
+        runs, and returns the pending record for finish_step()."""
         import torch
+        if not self._ready:
+            self._fill(self._slot)
+        slot = self._slot
+        start = torch.cuda.Event(enable_timing=True)
+        start.record()
+        self._batch.copy_(self._host[slot], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self._copied[slot] = ev
         m = self.model
-        losses = torch.zeros(self.n_micro, dtype=torch.float32, device=self.device)
         dloss = 1.0 / (self.B * self.T * self.n_micro)
         for k in range(self.n_micro):
-            tok, tgt = self.data.micro_batch(self.B, self.T)
-            m.forward(self._dev(tok), self._dev(tgt), dloss=dloss, loss_out=losses[k:k + 1])
+            m.forward(self._batch[k, 0], self._batch[k, 1], dloss=dloss, loss_out=self._loss[slot, k:k + 1])
             m.backward()
         lr = lr_at(self.step + 1)
-        norm = m.clip_adamw(lr, self.step + 1)
+        m.clip_adamw(lr, self.step + 1, norm_out=self._norm[slot:slot + 1])
+        end = torch.cuda.Event(enable_timing=True)
+        end.record()
         self.step += 1
-        return float(losses.mean().item()), float(norm.item()), lr
+        pending = {"step": self.step, "lr": lr, "slot": slot, "start": start, "end": end, "prev_end": self._last_end}
+        self._last_end = end
+        self._slot ^= 1
+        self._fill(self._slot)
+        self._ready = True
+        return pending
+
+    def finish_step(self, pending) -> dict:
+        """Waits for a launched step; returns its log record: mean training loss, norm
+        before clipping, lr and the step's tokens/s (end to end, from the previous
+        step's end, so host stalls between steps count)."""
+        pending["end"].synchronize()
+        slot = pending["slot"]
+        t0 = pending["prev_end"] or pending["start"]
+        ms = t0.elapsed_time(pending["end"])
+        return {"step": pending["step"], "lr": pending["lr"], "loss": float(self._loss[slot].mean().item()),
+                "grad_norm": float(self._norm[slot].item()),
+                "tokens_per_s": self.B * self.T * self.n_micro / (ms * 1e-3)}
+
+    def train_step(self):
+        """One optimizer step, waited for; returns (mean training loss, norm before clipping, lr)."""
+        r = self.finish_step(self.launch_step())
+        return r["loss"], r["grad_norm"], r["lr"]
 
     def held_out_batches(self, n: int):
-        """The same n held-out micro-batches at every evaluation (a stream of their own)."""
+        """The same n held-out micro-batches at every evaluation (a stream of their own),
+        uploaded once."""
+        import torch
         if self._eval is None or len(self._eval) < n:
             s = synth.TokenStream(self.V, self.eval_seed)
-            self._eval = [tuple(self._dev(a) for a in s.micro_batch(self.B, self.T)) for _ in range(n)]
+            self._eval = [tuple(torch.from_numpy(a).to(self.device) for a in s.micro_batch(self.B, self.T))
+                          for _ in range(n)]
         return self._eval[:n]
 
     def evaluate(self, n_batches: int = EVAL_BATCHES) -> float:
@@ -118,8 +178,9 @@ class Trainer:
         m = self.model
         for key, t in (("params", m.params), ("m", m.m), ("v", m.v)):
             np.save(os.path.join(tmp, key + ".npy"), t.detach().cpu().numpy())
+        cursor = self._cursor if self._ready else self.data.state()  # ids drawn ahead are drawn again
         meta = {"step": self.step, "workload": self.workload, "seed": self.seed, "eval_seed": self.eval_seed,
-                "data": self.data.state()}
+                "data": cursor}
         with open(os.path.join(tmp, "meta.json"), "w") as f:
             json.dump(meta, f)
         shutil.rmtree(final, ignore_errors=True)
@@ -149,8 +210,7 @@ class Trainer:
             t.copy_(torch.from_numpy(np.load(os.path.join(ck, key + ".npy"))).to(t.device))
         tr.data = synth.TokenStream.from_state(meta["data"])
         tr.step = int(meta["step"])
-        tr.device = torch.device(device)
-        tr._eval = None
+        tr._setup(device)
         return tr
 
     def run(self, run_dir: str, total_steps: int, eval_every: int = EVAL_EVERY, eval_batches: int = EVAL_BATCHES,
@@ -160,24 +220,42 @@ class Trainer:
         fail_at_step > 0 raises after that step (a forced crash, for relaunch tests)."""
         os.makedirs(run_dir, exist_ok=True)
         with open(os.path.join(run_dir, "log.jsonl"), "a") as logf:
-            while self.step < total_steps:
-                if os.path.exists(os.path.join(run_dir, HALT_MARKER)):
-                    log(f"halt marker at step {self.step}")
-                    return False
-                t0 = time.perf_counter()
-                loss, norm, lr = self.train_step()
-                dt = time.perf_counter() - t0
-                rec = {"step": self.step, "lr": lr, "loss": loss, "grad_norm": norm,
-                       "tokens_per_s": self.B * self.T * self.n_micro / dt}
-                if eval_every and self.step % eval_every == 0:
-                    rec["eval_loss"] = self.evaluate(eval_batches)
+            def write(rec):
                 logf.write(json.dumps(rec) + "\n")
                 logf.flush()
                 log(json.dumps(rec))
-                if ckpt_every and self.step % ckpt_every == 0:
-                    self.save(run_dir)
-                if fail_at_step and self.step == fail_at_step:
-                    raise RuntimeError(f"forced failure after step {self.step}")
+
+            def emit(pending):
+                rec = self.finish_step(pending)
+                if eval_every and rec["step"] % eval_every == 0:
+                    t0 = time.perf_counter()
+                    rec["eval_loss"] = self.evaluate(eval_batches)
+                    rec["eval_s"] = time.perf_counter() - t0
+                write(rec)
+
+            pending = None
+            while self.step < total_steps:
+                if os.path.exists(os.path.join(run_dir, HALT_MARKER)):
+                    if pending:
+                        emit(pending)
+                    log(f"halt marker at step {self.step}")
+                    return False
+                launched = self.launch_step()
+                if pending:
+                    emit(pending)
+                pending = launched
+                s = self.step
+                if (eval_every and s % eval_every == 0) or (ckpt_every and s % ckpt_every == 0) \
+                        or s == fail_at_step or s == total_steps:
+                    emit(pending)
+                    pending = None
+                    if ckpt_every and s % ckpt_every == 0:
+                        t0 = time.perf_counter()
+                        path = self.save(run_dir)
+                        write({"step": s, "checkpoint": os.path.basename(path), "save_s": time.perf_counter() - t0})
+                    if fail_at_step and s == fail_at_step:
+                        raise RuntimeError(f"forced failure after step {s}")
+                    self._last_end = None  # the next step's rate excludes the pause
         with open(os.path.join(run_dir, COMPLETE_MARKER), "w") as f:
             f.write(str(self.step))
         return True
