@@ -8,15 +8,15 @@ on a dependency-free stack:
 * held-out cross-entropy is the mean over 180 fixed batches, every 250 steps
   (evaluation paragraph);
 * checkpoints every 500 steps hold the parameters, the AdamW moments, the step
-  and the data cursor, so a restart resumes rather than repeats; a supervisor
-  relaunches a crashed run from its latest checkpoint and stops for good on a
-  completion or a halt marker (supervision paragraph).
+  and the data cursor, so a restart resumes rather than repeats (supervision
+  paragraph); the supervisor and the halting gate are in supervisor.py.
 
 Data are synthetic (synth.TokenStream: a Zipf/end-of-text stream standing in
 for the FineWeb shards).  Every GPU operation is a call into libgpt2mi.so.
 
     python -m transformer_lm_pretraining_amd.train --run-dir runs/a --steps 1000
     python -m transformer_lm_pretraining_amd.train --run-dir runs/a --steps 1000 --supervise
+    python -m transformer_lm_pretraining_amd.train --run-dir runs/a --sidecar reference.json
 """
 from __future__ import annotations
 
@@ -25,13 +25,13 @@ import json
 import math
 import os
 import shutil
-import subprocess
 import sys
 import time
 
 import numpy as np
 
 from . import lib, synth
+from .supervisor import COMPLETE_MARKER, HALT_MARKER, load_reference, sidecar, supervise
 
 MAX_LR = 6e-4
 WARMUP_STEPS = 700
@@ -39,8 +39,6 @@ TOTAL_STEPS = 18865
 EVAL_EVERY = 250
 EVAL_BATCHES = 180
 CKPT_EVERY = 500
-COMPLETE_MARKER = "COMPLETE"
-HALT_MARKER = "HALT"
 
 WORKLOADS = {
     # name: (L, H, C, V, Vp, Tmax, B, T, n_micro)
@@ -261,29 +259,10 @@ class Trainer:
         return True
 
 
-def supervise(cmd, run_dir: str, max_restarts: int = 10, log=print) -> int:
-    """Runs `cmd` (a list) until it leaves the completion marker in run_dir; relaunches it
-    after a failure (the trainer resumes from run_dir/latest itself); stops for good,
-    without launching, once a halt or completion marker exists.  Returns the number of
-    launches."""
-    launches = 0
-    while True:
-        for marker in (HALT_MARKER, COMPLETE_MARKER):
-            if os.path.exists(os.path.join(run_dir, marker)):
-                log(f"supervisor: {marker} marker present, stopping after {launches} launch(es)")
-                return launches
-        if launches > max_restarts:
-            log(f"supervisor: giving up after {launches} launches")
-            return launches
-        launches += 1
-        rc = subprocess.call(cmd)
-        log(f"supervisor: launch {launches} exited with {rc}")
-
-
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--run-dir", required=True)
-    ap.add_argument("--steps", type=int, required=True, help="total optimizer steps of the run")
+    ap.add_argument("--steps", type=int, help="total optimizer steps of the run")
     ap.add_argument("--workload", default="gpt2_124m", choices=sorted(WORKLOADS))
     ap.add_argument("--eval-every", type=int, default=EVAL_EVERY)
     ap.add_argument("--eval-batches", type=int, default=EVAL_BATCHES)
@@ -293,7 +272,15 @@ def main(argv=None):
     ap.add_argument("--max-restarts", type=int, default=10)
     ap.add_argument("--fail-at-step", type=int, default=0,
                     help="on a fresh start, crash after this step (relaunch tests)")
+    ap.add_argument("--sidecar", metavar="REFERENCE_JSON",
+                    help="run the halting gate on run-dir against a {step: held-out loss} reference curve")
+    ap.add_argument("--gate-interval", type=float, default=300.0, help="seconds between gate checks")
     a = ap.parse_args(argv)
+    if a.sidecar:
+        print(sidecar(a.run_dir, load_reference(a.sidecar), a.gate_interval, log=lambda s: print(s, flush=True)))
+        return 0
+    if a.steps is None:
+        ap.error("--steps is required to train")
     if a.supervise:
         child = [sys.executable, "-m", "transformer_lm_pretraining_amd.train"] + \
                 [x for x in (argv if argv is not None else sys.argv[1:]) if x != "--supervise"]
