@@ -264,6 +264,26 @@ def test_gpt2_shapes_two_layers_parity(gpu_lib, L, B):
     check_grads(grad_dict(model, cfg), G, cfg, T)
 
 
+def test_wide_shapes_two_layers_parity(gpu_lib):
+    """The wider model's layer shapes (C=1536, 24 heads of 64, MLP 6144, T=1024, vocabulary
+    8,449 padded to 8,576) at 2 layers, B=1: loss and every gradient against the oracle."""
+    import torch
+    cfg = Config(L=2, H=24, C=1536, V=8449, Vp=8576, Tmax=1024)
+    B, T = 1, 1024
+    say("wide-shape layers", cfg.L, "batch", B)
+    P = init_params(cfg, 1337)
+    tok, tgt = synth.micro_batches(1, B, T, cfg.V, seed=23)[0]
+    assert tok.max() == cfg.V - 1 and tok.max() < cfg.V  # end-of-text is the last real id
+    model = make_model(cfg, B, T, init=oracle.flatten(cfg, P))
+    loss = model.forward(to_dev_i32(tok), to_dev_i32(tgt), dloss=1.0 / (B * T))
+    model.backward()
+    torch.cuda.synchronize()
+    ref_loss, G, _ = loss_and_grads(cfg, P, tok, tgt, dtype=np.float32)
+    say("loss gpu", float(loss.item()), "oracle", ref_loss)
+    assert abs(float(loss.item()) - ref_loss) <= 2e-2
+    check_grads(grad_dict(model, cfg), G, cfg, T)
+
+
 def test_gpt2_124m_full_size_sampled(gpu_lib):
     """Full 124M model at one card's micro-batch (19 x 1024): per-sequence losses of
     sampled sequences against the oracle, plus gradient properties."""
