@@ -29,6 +29,11 @@
  * and gpt2_eval_loss report (GPT2_E_DATA).  Such ids are clamped into range
  * so every kernel stays in bounds.
  *
+ * Reproducibility: every sum in the step has a fixed order (no floating-point
+ * atomics whose order depends on scheduling), so the same weights, moments,
+ * batch and arguments give the same bits on every run of a given build and
+ * device; a run restored from its saved state continues exactly.
+ *
  * Data types: bf16 values are passed as uint16_t bit patterns (round to
  * nearest even).  Token and target ids are int32.
  */

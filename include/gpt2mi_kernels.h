@@ -45,7 +45,8 @@ int gpt2k_layernorm_fwd(const uint16_t* x, const float* w, const float* b, uint1
  * LayerNorm backward.  dx = rstd (w dy - mean(w dy) - xhat mean(w dy xhat));
  * dres (bf16 [rows, C]) <- dx if accumulate == 0, else dres + dx (the
  * residual-stream gradient).  dw += sum_rows dy xhat; db += sum_rows dy
- * (fp32 [C], accumulated).  scratch: at least gpt2k_scratch_bytes(1, rows, C, 0).
+ * (fp32 [C], accumulated; the sums have a fixed order, so the same inputs give
+ * the same bits).  scratch: at least gpt2k_scratch_bytes(1, rows, C, 0).
  */
 int gpt2k_layernorm_bwd(const uint16_t* x, const uint16_t* dy, const float* w, const float* mean,
                         const float* rstd, uint16_t* dres, int32_t accumulate, float* dw, float* db, void* scratch,
@@ -78,7 +79,8 @@ int gpt2k_bias_gelu_bwd(const uint16_t* pre, const uint16_t* dg, uint16_t* dpre,
  *  gpt2k_gemm_tn_acc: dW[N, K] += sum_m dY[m, n] X[m, k] (fp32 dW, bf16
  *    dY [M, N] and X [M, K]) and, if db != NULL, db[n] += sum_m dY[m, n]
  *    (fp32, the bias gradient); M % 64 == 0.  scratch: gpt2k_scratch_bytes(3,
- *    M, N, K) (split-K partials).
+ *    M, N, K) (split-K partials and their bias column sums, added in split
+ *    order: the same inputs give the same bits).
  */
 int gpt2k_gemm_nt(const uint16_t* A, const uint16_t* B, const float* bias, const uint16_t* res, uint16_t* out,
                   int64_t M, int64_t N, int64_t K, hipStream_t stream);
@@ -135,9 +137,10 @@ int gpt2k_embedding_fwd(const int32_t* tok, const uint16_t* wte, const uint16_t*
 /*
  * Embedding backward: dwte[tok[r]] += dx[r]; dwpe[t] += sum_b dx[b*T + t]
  * (fp32 tables, bf16 dx).  Ids outside [0, V) are skipped.  scratch: device
- * bytes, at least gpt2k_scratch_bytes(5, B*T, V) (the rows are counting-sorted
- * by token there); too small -> GPT2_E_SHAPE.  The additions into a table row
- * come in no fixed order (runs that cross a sorting window add atomically).
+ * bytes, 16-byte aligned, at least gpt2k_scratch_bytes(5, B*T, V, C) (the rows
+ * are counting-sorted by token there); too small -> GPT2_E_SHAPE.  The rows of
+ * a token are added in increasing row order, in windows of 32 whose partial
+ * sums are then added in window order: the result is the same bits every run.
  */
 int gpt2k_embedding_bwd(const int32_t* tok, const uint16_t* dx, float* dwte, float* dwpe, int32_t B, int32_t T,
                         int32_t C, int32_t V, void* scratch, int64_t scratch_bytes, hipStream_t stream);
@@ -146,7 +149,7 @@ int gpt2k_embedding_bwd(const int32_t* tok, const uint16_t* dx, float* dwte, flo
  * Scratch bytes needed by the kernel-level calls, written to *out:
  * kind 1 = layernorm_bwd (a = rows, b = C); kind 2 = bias_gelu_bwd or
  * bias_grad (a = rows, b = N); kind 3 = gemm_tn_acc (a = M, b = N, c = K);
- * kind 4 = clip_adamw (a = n); kind 5 = embedding_bwd (a = B*T, b = V).
+ * kind 4 = clip_adamw (a = n); kind 5 = embedding_bwd (a = B*T, b = V, c = C).
  * Unused arguments are ignored.
  */
 int gpt2k_scratch_bytes(int32_t kind, int64_t a, int64_t b, int64_t c, int64_t* out);

@@ -362,7 +362,8 @@ def test_embedding_parity(gpu_lib):
 def test_embedding_bwd_hot_tokens_and_invalid_ids(gpu_lib):
     """Token-table scatter at the full batch (Zipf ids: token 0 covers ~14% of rows), plus
     a batch where one id fills 300 rows (runs crossing many sorting windows) and ids
-    outside [0, V) that must be skipped, and a batch of 71,680 rows (two sort chunks)."""
+    outside [0, V) that must be skipped, and a batch of 71,680 rows (two sort chunks).
+    A second call gives the same bits (the rows of a token are summed in a fixed order)."""
     import torch
     from transformer_lm_pretraining_amd import lib
     V, Vp = 50257, 50304
@@ -395,6 +396,10 @@ def test_embedding_bwd_hot_tokens_and_invalid_ids(gpu_lib):
         np.testing.assert_allclose(host(dwte), rw, rtol=1e-5, atol=1e-4)
         np.testing.assert_allclose(host(dwpe), rp, rtol=1e-5, atol=1e-5)
         assert np.all(host(dwte)[V:] == 0)
+        again = to_dev_f32(np.zeros((Vp, C)))
+        lib.embedding_bwd(to_dev_i32(tok), to_dev_bf16(dx), again, to_dev_f32(np.zeros((T, C))), V)
+        torch.cuda.synchronize()
+        assert torch.equal(dwte, again)
 
 
 # ---------------------------------------------------------------- clip + AdamW

@@ -264,6 +264,36 @@ def test_gpt2_shapes_two_layers_parity(gpu_lib, L, B):
     check_grads(grad_dict(model, cfg), G, cfg, T)
 
 
+@pytest.mark.parametrize("shape", ["tiny", "gpt2_layers"])
+def test_step_is_bitwise_reproducible(gpu_lib, shape):
+    """Two models from the same weights and batch end a step (forward, backward,
+    clip + AdamW) with the same bits: every sum in the step has a fixed order
+    (LayerNorm and bias gradients, split weight-gradient reductions and the
+    token-table gradient included)."""
+    import torch
+    if shape == "tiny":
+        cfg, B, T = CONFIGS["tiny"], 4, 64
+    else:
+        cfg, B, T = Config(L=2, H=12, C=768, V=50257, Vp=50304, Tmax=1024), 2, 1024
+    say("reproducible step", shape)
+    flat = oracle.flatten(cfg, init_params(cfg, 1337))
+    batches = synth.micro_batches(2, B, T, cfg.V, seed=29)
+    runs = []
+    for _ in range(2):
+        model = make_model(cfg, B, T, init=flat)
+        for tok, tgt in batches:
+            model.forward(to_dev_i32(tok), to_dev_i32(tgt), dloss=1.0 / (2 * B * T))
+            model.backward()
+        grads = model.grads.clone()
+        norm = model.clip_adamw(oracle.lr_at(350), 1)
+        torch.cuda.synchronize()
+        runs.append((grads.cpu().numpy(), model.params.cpu().numpy(), float(norm.item())))
+        del model
+    (g0, p0, n0), (g1, p1, n1) = runs
+    assert np.array_equal(g0, g1), int(np.sum(g0 != g1))
+    assert np.array_equal(p0, p1) and n0 == n1
+
+
 def test_wide_shapes_two_layers_parity(gpu_lib):
     """The wider model's layer shapes (C=1536, 24 heads of 64, MLP 6144, T=1024, vocabulary
     8,449 padded to 8,576) at 2 layers, B=1: loss and every gradient against the oracle."""

@@ -196,7 +196,7 @@ ScratchPlan plan_scratch(const gpt2_config& c) {
     off = align_up(off + s.splitk_elems * 4);
     s.dvec = off;
     off = align_up(off + (int64_t)c.B * c.H * c.T * 4);
-    s.emb_work_elems = embedding_bwd_work_elems(BT, c.V);
+    s.emb_work_elems = embedding_bwd_work_elems(BT, c.V, c.C);
     s.emb_work = off;
     off = align_up(off + s.emb_work_elems * 4);
     s.total = off;
@@ -694,7 +694,7 @@ int gpt2k_scratch_bytes(int32_t kind, int64_t a, int64_t b, int64_t c, int64_t* 
         case 2: *out = colsum_partial_elems(a, (int)b) * 4; return GPT2_OK;
         case 3: *out = gemm_tn_partial_elems((int)a, (int)b, (int)c) * 4; return GPT2_OK;
         case 4: *out = adamw_partial_elems(a) * 8 + 256; return GPT2_OK;
-        case 5: *out = embedding_bwd_work_elems(a, (int)b) * 4; return GPT2_OK;
+        case 5: *out = embedding_bwd_work_elems(a, (int)b, (int)c) * 4; return GPT2_OK;
     }
     return GPT2_E_INVALID;
 }
@@ -826,7 +826,7 @@ int gpt2k_embedding_bwd(const int32_t* tok, const uint16_t* dx, float* dwte, flo
     if (!tok || !dx || !dwte || !dwpe || !scratch || B < 1 || T < 1 || C < 8 || C % 8 || V < 1 ||
         (int64_t)B * T > INT32_MAX)
         return GPT2_E_INVALID;
-    if (scratch_bytes < embedding_bwd_work_elems((int64_t)B * T, V) * 4) return GPT2_E_SHAPE;
+    if (scratch_bytes < embedding_bwd_work_elems((int64_t)B * T, V, C) * 4) return GPT2_E_SHAPE;
     KCHK(launch_embedding_bwd(tok, dx, dwte, dwpe, B, T, C, V, (int32_t*)scratch, scratch_bytes / 4, s));
     return GPT2_OK;
 }

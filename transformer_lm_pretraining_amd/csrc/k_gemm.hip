@@ -963,8 +963,15 @@ bool tn_tail_plan(int N, int K, int nk, int* full_rows, int* tail_splits) {
     return true;
 }
 
+// Column-sum partials for the bias gradients of a split launch (one product at a time).
+int64_t tn_bias_partial_elems(const TnJobDesc* jobs, int n, int M) {
+    int64_t e = 0;
+    for (int j = 0; j < n; ++j) e = std::max(e, colsum_partial_elems(M, jobs[j].N));
+    return e;
+}
+
 // Runs jobs [0, n) of equal token count M as one grouped 256x256-tile launch
-// (plus one reduce launch when split).
+// (plus one reduce launch, and the bias column sums, when split).
 hipError_t run_tn_group(const TnJobDesc* jobs, int n, int M, float* partial, int64_t partial_elems, hipStream_t s) {
     TnGroup G{};
     G.njobs = n;
@@ -984,7 +991,7 @@ hipError_t run_tn_group(const TnJobDesc* jobs, int n, int M, float* partial, int
     }
     G.tile_start[n] = (int)tiles;
     int sp = tn_group_splits(tiles, G.nk_total);
-    if (sp > 1 && (partial == nullptr || partial_elems < sp * elems)) sp = 1;
+    if (sp > 1 && (partial == nullptr || partial_elems < sp * elems + tn_bias_partial_elems(jobs, n, M))) sp = 1;
     G.splits = sp;
     if (sp == 1) {
         for (int j = 0; j < n; ++j) G.job[j].out = jobs[j].dW;
@@ -1000,6 +1007,9 @@ hipError_t run_tn_group(const TnJobDesc* jobs, int n, int M, float* partial, int
     for (int j = 0; j < n; ++j) {
         const int64_t e = (int64_t)jobs[j].N * jobs[j].K;
         G.job[j].out = partial + off;
+        // the splits of a product would add into each bias row in no fixed order:
+        // its bias gradient is summed afterwards by the column-sum kernel instead
+        G.job[j].dbias = nullptr;
         R.part[j] = (const float4*)(partial + off);
         R.dw[j] = (float4*)jobs[j].dW;
         R.start4[j + 1] = R.start4[j] + e / 4;
@@ -1014,7 +1024,10 @@ hipError_t run_tn_group(const TnJobDesc* jobs, int n, int M, float* partial, int
     const int blocks = (int)std::min<int64_t>(cdiv(n4, 256), 4096);
     PROF_LAUNCH(KC_SPLITK_REDUCE, 16.0 * n4 * (sp + 2), s,
                 hipLaunchKernelGGL(splitk_reduce_group_kernel, dim3(blocks), dim3(256), 0, s, R));
-    return hipGetLastError();
+    e = hipGetLastError();
+    for (int j = 0; j < n && e == hipSuccess; ++j)
+        if (jobs[j].db != nullptr) e = launch_bias_grad(jobs[j].dY, jobs[j].ldy, jobs[j].db, partial + off, M, jobs[j].N, s);
+    return e;
 }
 
 }  // namespace
@@ -1095,15 +1108,20 @@ hipError_t launch_gemm_tn_group(const TnJobDesc* jobs, int n, int M, float* part
     return hipSuccess;
 }
 
+// Split partials of a launch (splits x N x K per product) plus the column-sum
+// partials of its bias gradients.
 int64_t gemm_tn_group_partial_elems(const TnJobDesc* jobs, int n, int M) {
     int full_rows = 0, tail_sp = 1;
     if (n == 1 && tn_tail_plan(jobs[0].N, jobs[0].K, M / BK, &full_rows, &tail_sp))
-        return (int64_t)tail_sp * (jobs[0].N - full_rows) * jobs[0].K;
+        return (int64_t)tail_sp * (jobs[0].N - full_rows) * jobs[0].K + colsum_partial_elems(M, jobs[0].N - full_rows);
     int hi[TN_MAX_JOBS], ti[TN_MAX_JOBS], nh = 0, nt = 0;
     if (n <= TN_MAX_JOBS && tn_group_tail_plan(jobs, n, M / BK, hi, &nh, ti, &nt, &tail_sp)) {
-        int64_t e = 0;
-        for (int i = 0; i < nt; ++i) e += (int64_t)jobs[ti[i]].N * jobs[ti[i]].K;
-        return tail_sp * e;
+        int64_t e = 0, b = 0;
+        for (int i = 0; i < nt; ++i) {
+            e += (int64_t)jobs[ti[i]].N * jobs[ti[i]].K;
+            b = std::max(b, colsum_partial_elems(M, jobs[ti[i]].N));
+        }
+        return tail_sp * e + b;
     }
     int64_t tiles = 0, elems = 0;
     for (int j = 0; j < n; ++j) {
@@ -1111,5 +1129,5 @@ int64_t gemm_tn_group_partial_elems(const TnJobDesc* jobs, int n, int M) {
         elems += (int64_t)jobs[j].N * jobs[j].K;
     }
     const int sp = tn_group_splits(tiles, M / BK);
-    return sp > 1 ? sp * elems : 0;
+    return sp > 1 ? sp * elems + tn_bias_partial_elems(jobs, n, M) : 0;
 }

@@ -57,7 +57,28 @@ __global__ __launch_bounds__(CS_THREADS) void colsum_kernel(const uint16_t* __re
     for (int q = 0; q < CS_MAXV; ++q)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
-    for (int64_t r = r0; r < r1; ++r) {
+    int64_t r = r0;
+    if constexpr (!GELU_BWD) {
+        // four rows' loads in flight, added in row order
+        for (; r + 4 <= r1; r += 4) {
+#pragma unroll
+            for (int q = 0; q < CS_MAXV; ++q) {
+                const int cv = threadIdx.x + CS_THREADS * q;
+                if (cv >= nv) break;
+                u32x4 w[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) w[u] = *(const u32x4*)(src + (r + u) * lds + cv * 8);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[q][2 * e] += bflo(w[u][e]);
+                        acc[q][2 * e + 1] += bfhi(w[u][e]);
+                    }
+            }
+        }
+    }
+    for (; r < r1; ++r) {
 #pragma unroll
         for (int q = 0; q < CS_MAXV; ++q) {
             const int cv = threadIdx.x + CS_THREADS * q;
@@ -270,24 +291,32 @@ __global__ __launch_bounds__(256) void embedding_fwd_kernel(const int32_t* __res
     }
 }
 
-// Token-table gradient: the rows are counting-sorted by token id (one
-// workgroup: count, scan and scatter in LDS), then each wave sums a window of
-// EMB_WIN sorted rows run by run, for a chunk of columns.  A token occurring N times (Zipf: the most frequent id covers ~14% of a
-// batch) then costs about N / EMB_WIN additions to its table row instead of N
-// contending atomics.  A run that lies inside one window is the only writer of
-// its table row and read-modify-writes it; a run that crosses a window edge
-// adds atomically.  Ids outside [0, V) are left out.
+// Token-table gradient, with every addition in a fixed order (the same bits on
+// every run).  (1) The rows are counting-sorted by token id in one workgroup
+// (count, scan and scatter in LDS); the scan also leaves each token's bucket
+// start in global memory.  (2) Within each bucket the rows are put in
+// increasing row order (a row's place is the number of smaller row ids in its
+// bucket).  (3) Each wave sums a window of EMB_WIN sorted rows run by run, for a
+// chunk of columns.  A run inside one window is the only writer of its table
+// row and read-modify-writes it; the pieces of a run that crosses window edges
+// go to per-window scratch (H: the window's first run, T: its last run).
+// (4) One pass adds each crossing run's pieces, window by window, into its
+// table row.  A token occurring N times (Zipf: the most frequent id covers ~14%
+// of a batch) costs about N / EMB_WIN additions to its table row.  Ids outside
+// [0, V) are left out.
 constexpr int EMB_WIN = 32;
 
 // Counting sort of the row ids by token in one workgroup, all in LDS: 16-bit
-// counts packed two per word (a batch has fewer than 65,536 rows), counted with
-// LDS atomics, scanned in place into start offsets, then advanced by the
-// scatter.  Writes order[] / stok[] (row index and token of each sorted
-// position) and n = number of valid rows to *nvalid.
+// counts packed two per word (a chunk has fewer than 65,536 rows), counted with
+// LDS atomics, scanned in place into start offsets (also written to bstart[0..V],
+// bstart[V] = number of valid rows), then advanced by the scatter.  Writes
+// order[] / stok[] (row index and token of each sorted position; the order
+// within a bucket is not yet fixed) and the valid row count to *nvalid.
 constexpr int EMB_SORT_THREADS = 1024;
 __global__ __launch_bounds__(EMB_SORT_THREADS) void emb_sort_kernel(const int32_t* __restrict__ tok, int rows, int V,
                                                                     int32_t* __restrict__ order,
                                                                     int32_t* __restrict__ stok,
+                                                                    int32_t* __restrict__ bstart,
                                                                     int32_t* __restrict__ nvalid) {
     __shared__ uint32_t cnt[32768];  // counts of token t in half (t & 1) of word t >> 1
     __shared__ int wtot[EMB_SORT_THREADS / 64];
@@ -322,7 +351,12 @@ __global__ __launch_bounds__(EMB_SORT_THREADS) void emb_sort_kernel(const int32_
         run = (int)hi + (int)(c >> 16);
         cnt[w] = lo | (hi << 16);
     }
-    if (tid == EMB_SORT_THREADS - 1) *nvalid = run;
+    if (tid == EMB_SORT_THREADS - 1) {
+        *nvalid = run;
+        bstart[V] = run;
+    }
+    __syncthreads();
+    for (int t = tid; t < V; t += EMB_SORT_THREADS) bstart[t] = (int)((cnt[t >> 1] >> ((t & 1) * 16)) & 0xffffu);
     __syncthreads();
     for (int i = tid; i < rows; i += EMB_SORT_THREADS) {
         const int t = tok[i];
@@ -334,13 +368,55 @@ __global__ __launch_bounds__(EMB_SORT_THREADS) void emb_sort_kernel(const int32_
     }
 }
 
+// Sorted position p of bucket [s, e) takes the row whose id has rank p - s among
+// the bucket's ids (ids in a bucket are distinct), from the scatter's order.  A
+// block of 256 positions copies the ids of every bucket it touches into LDS
+// (EMB_RANK_TILE at a time, all loads in flight); each thread counts the smaller
+// ids inside its own bucket, four per LDS read where the range allows.
+constexpr int EMB_RANK_TILE = 8192;
+__global__ __launch_bounds__(256) void emb_rank_kernel(const int32_t* __restrict__ scattered,
+                                                       const int32_t* __restrict__ stok,
+                                                       const int32_t* __restrict__ bstart,
+                                                       const int32_t* __restrict__ nvalid,
+                                                       int32_t* __restrict__ order) {
+    __shared__ int4 ids4[EMB_RANK_TILE / 4];
+    const int* ids = (const int*)ids4;
+    const int n = *nvalid;
+    const int b0 = blockIdx.x * 256;
+    if (b0 >= n) return;
+    const int b1 = min(b0 + 256, n);
+    const int p = b0 + threadIdx.x;
+    const bool live = p < n;
+    const int t = stok[live ? p : b0];
+    const int s = bstart[t], e = bstart[t + 1];
+    const int my = live ? scattered[p] : 0;
+    const int u0 = bstart[stok[b0]], u1 = bstart[stok[b1 - 1] + 1];  // the buckets this block touches
+    int rank = 0;
+    for (int q0 = u0; q0 < u1; q0 += EMB_RANK_TILE) {
+        const int m = min(EMB_RANK_TILE, u1 - q0);
+        __syncthreads();
+        for (int i = threadIdx.x; i < m; i += 256) ((int*)ids4)[i] = scattered[q0 + i];
+        __syncthreads();
+        int k = max(s - q0, 0);
+        const int k1 = min(e - q0, m);
+        for (; k < k1 && (k & 3); ++k) rank += ids[k] < my ? 1 : 0;
+#pragma unroll 8
+        for (; k + 4 <= k1; k += 4) {
+            const int4 v = ids4[k >> 2];
+            rank += (v.x < my ? 1 : 0) + (v.y < my ? 1 : 0) + (v.z < my ? 1 : 0) + (v.w < my ? 1 : 0);
+        }
+        for (; k < k1; ++k) rank += ids[k] < my ? 1 : 0;
+    }
+    if (live) order[s + rank] = my;
+}
+
 // One wave per (window of EMB_WIN sorted rows, chunk of 256 columns); each lane
-// owns 4 columns.
+// owns 4 columns.  part: [window][2][C] floats (H, then T).
 __global__ __launch_bounds__(256) void emb_segsum_kernel(const int32_t* __restrict__ order,
                                                          const int32_t* __restrict__ stok,
                                                          const int32_t* __restrict__ nvalid,
                                                          const uint16_t* __restrict__ dx, int C,
-                                                         float* __restrict__ dwte) {
+                                                         float* __restrict__ dwte, float* __restrict__ part) {
     const int n = *nvalid;
     const int nch = (C / 4 + 63) / 64;
     const int wid = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * 256 + threadIdx.x) >> 6));
@@ -351,46 +427,84 @@ __global__ __launch_bounds__(256) void emb_segsum_kernel(const int32_t* __restri
     const int p1 = min(p0 + EMB_WIN, n);
     const bool head_shared = p0 > 0 && stok[p0 - 1] == stok[p0];
     const bool tail_shared = p1 < n && stok[p1] == stok[p1 - 1];
-    {
-        const int c4 = ch * 64 + lane;
-        if (c4 >= C / 4) return;
-        u32x2 gv[EMB_WIN];
+    const int c4 = ch * 64 + lane;
+    if (c4 >= C / 4) return;
+    u32x2 gv[EMB_WIN];
 #pragma unroll
-        for (int q = 0; q < EMB_WIN; ++q)
-            if (p0 + q < p1) gv[q] = *(const u32x2*)(dx + (int64_t)order[p0 + q] * C + c4 * 4);
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        int cur = stok[p0];
-        bool shared = head_shared;
-        auto flush = [&](bool sh) {
+    for (int q = 0; q < EMB_WIN; ++q)
+        if (p0 + q < p1) gv[q] = *(const u32x2*)(dx + (int64_t)order[p0 + q] * C + c4 * 4);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int cur = stok[p0];
+    bool first = true;
+    // a run piece goes to H (first run, continuing from the previous window), to T
+    // (last run, continuing into the next window) or, whole, into its table row
+    auto flush = [&](bool last) {
+        if (first && head_shared) {
+            *(float4*)(part + (int64_t)(2 * wv) * C + c4 * 4) = acc;
+        } else if (last && tail_shared) {
+            *(float4*)(part + (int64_t)(2 * wv + 1) * C + c4 * 4) = acc;
+        } else {
             float* d = dwte + (int64_t)cur * C + c4 * 4;
-            if (sh) {
-                unsafeAtomicAdd(d, acc.x);
-                unsafeAtomicAdd(d + 1, acc.y);
-                unsafeAtomicAdd(d + 2, acc.z);
-                unsafeAtomicAdd(d + 3, acc.w);
-            } else {
-                float4 o = *(float4*)d;
-                o.x += acc.x; o.y += acc.y; o.z += acc.z; o.w += acc.w;
-                *(float4*)d = o;
-            }
-        };
-#pragma unroll
-        for (int q = 0; q < EMB_WIN; ++q) {
-            if (p0 + q >= p1) break;
-            const int t = stok[p0 + q];
-            if (t != cur) {
-                flush(shared);
-                acc = make_float4(0.f, 0.f, 0.f, 0.f);
-                cur = t;
-                shared = false;
-            }
-            acc.x += bflo(gv[q].x);
-            acc.y += bfhi(gv[q].x);
-            acc.z += bflo(gv[q].y);
-            acc.w += bfhi(gv[q].y);
+            float4 o = *(float4*)d;
+            o.x += acc.x; o.y += acc.y; o.z += acc.z; o.w += acc.w;
+            *(float4*)d = o;
         }
-        flush(shared || tail_shared);
+    };
+#pragma unroll
+    for (int q = 0; q < EMB_WIN; ++q) {
+        if (p0 + q >= p1) break;
+        const int t = stok[p0 + q];
+        if (t != cur) {
+            flush(false);
+            acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            cur = t;
+            first = false;
+        }
+        acc.x += bflo(gv[q].x);
+        acc.y += bfhi(gv[q].x);
+        acc.z += bflo(gv[q].y);
+        acc.w += bfhi(gv[q].y);
     }
+    flush(true);
+}
+
+// A run that crosses window edges, from the window where it starts: its piece
+// there (T), the whole windows it spans and its piece in the window where it
+// ends (H; that window holds the bucket's last row), added in window order, then
+// into its table row.  Block (w, y): window w, 64 column vectors of 4.
+__global__ __launch_bounds__(64) void emb_combine_kernel(const int32_t* __restrict__ stok,
+                                                         const int32_t* __restrict__ bstart,
+                                                         const int32_t* __restrict__ nvalid, int C,
+                                                         const float* __restrict__ part, float* __restrict__ dwte) {
+    const int n = *nvalid;
+    const int w = blockIdx.x;
+    const int p0 = w * EMB_WIN, p1 = min(p0 + EMB_WIN, n);
+    if (p0 >= n) return;
+    if (!(p1 < n && stok[p1] == stok[p1 - 1])) return;                           // last run ends here
+    if (p0 > 0 && stok[p0 - 1] == stok[p0] && stok[p0] == stok[p1 - 1]) return;  // it started earlier
+    const int c4 = blockIdx.y * 64 + threadIdx.x;
+    if (c4 >= C / 4) return;
+    const int t = stok[p1 - 1];
+    const int wlast = (bstart[t + 1] - 1) / EMB_WIN;
+    float4 acc = *(const float4*)(part + (int64_t)(2 * w + 1) * C + c4 * 4);
+    int w2 = w + 1;
+    for (; w2 + 8 <= wlast + 1; w2 += 8) {  // eight loads in flight, added in window order
+        float4 h[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) h[u] = *(const float4*)(part + (int64_t)(2 * (w2 + u)) * C + c4 * 4);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            acc.x += h[u].x; acc.y += h[u].y; acc.z += h[u].z; acc.w += h[u].w;
+        }
+    }
+    for (; w2 <= wlast; ++w2) {
+        const float4 h = *(const float4*)(part + (int64_t)(2 * w2) * C + c4 * 4);
+        acc.x += h.x; acc.y += h.y; acc.z += h.z; acc.w += h.w;
+    }
+    float* d = dwte + (int64_t)t * C + c4 * 4;
+    float4 o = *(float4*)d;
+    o.x += acc.x; o.y += acc.y; o.z += acc.z; o.w += acc.w;
+    *(float4*)d = o;
 }
 
 __global__ __launch_bounds__(256) void embedding_bwd_wpe_kernel(const uint16_t* __restrict__ dx,
@@ -474,26 +588,44 @@ hipError_t launch_embedding_fwd(const int32_t* tok, const uint16_t* wte, const u
     return hipGetLastError();
 }
 
-int64_t embedding_bwd_work_elems(int64_t rows, int V) { return 3 * (int64_t)V + 1 + 2 * rows; }
+namespace {
+constexpr int64_t EMB_CHUNK = 65535;  // the sort keeps 16-bit offsets: larger batches go in chunks
+// work: nvalid (+ 3 pad), scattered ids, sorted ids, sorted tokens (nmax each), bucket starts
+// (V + 1), then the window pieces (floats) from the next 16-byte boundary
+int64_t emb_part_offset(int64_t nmax, int V) { return (4 + 3 * nmax + V + 1 + 3) / 4 * 4; }
+}  // namespace
+
+int64_t embedding_bwd_work_elems(int64_t rows, int V, int C) {
+    const int64_t nmax = std::min(rows, EMB_CHUNK);
+    return emb_part_offset(nmax, V) + 2 * cdiv(nmax, EMB_WIN) * C;
+}
 
 hipError_t launch_embedding_bwd(const int32_t* tok, const uint16_t* dx, float* dwte, float* dwpe, int B, int T,
                                 int C, int V, int32_t* work, int64_t work_elems, hipStream_t s) {
     const int64_t rows = (int64_t)B * T;
-    if (C % 4 || V > 65536 || work == nullptr || work_elems < embedding_bwd_work_elems(rows, V) || rows > INT32_MAX)
+    if (C % 4 || V > 65536 || work == nullptr || work_elems < embedding_bwd_work_elems(rows, V, C) ||
+        rows > INT32_MAX)
         return hipErrorInvalidValue;
-    // the sort keeps 16-bit offsets: batches of more rows go in chunks
-    constexpr int64_t CHUNK = 65535;
+    const int64_t nmax = std::min(rows, EMB_CHUNK);
     int32_t* nvalid = work;
-    int32_t* order = work + 1;
-    int32_t* stok = order + std::min(rows, CHUNK);
-    for (int64_t r0 = 0; r0 < rows; r0 += CHUNK) {
-        const int64_t n = std::min(CHUNK, rows - r0);
-        const int64_t nwaves = cdiv(n, EMB_WIN) * cdiv(C / 4, 64);
+    int32_t* scattered = work + 4;
+    int32_t* order = scattered + nmax;
+    int32_t* stok = order + nmax;
+    int32_t* bstart = stok + nmax;
+    float* part = (float*)(work + emb_part_offset(nmax, V));
+    for (int64_t r0 = 0; r0 < rows; r0 += EMB_CHUNK) {
+        const int64_t n = std::min(EMB_CHUNK, rows - r0);
+        const int64_t nwin = cdiv(n, EMB_WIN);
+        const int64_t nwaves = nwin * cdiv(C / 4, 64);
         PROF_LAUNCH(KC_EMB_BWD_WTE, 4.0 * n * C + 8.0 * n * C, s, {
-            hipLaunchKernelGGL(emb_sort_kernel, dim3(1), dim3(EMB_SORT_THREADS), 0, s, tok + r0, (int)n, V, order,
-                               stok, nvalid);
+            hipLaunchKernelGGL(emb_sort_kernel, dim3(1), dim3(EMB_SORT_THREADS), 0, s, tok + r0, (int)n, V, scattered,
+                               stok, bstart, nvalid);
+            hipLaunchKernelGGL(emb_rank_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, scattered, stok, bstart,
+                               nvalid, order);
             hipLaunchKernelGGL(emb_segsum_kernel, dim3((unsigned)cdiv(nwaves, 4)), dim3(256), 0, s, order, stok,
-                               nvalid, dx + r0 * C, C, dwte);
+                               nvalid, dx + r0 * C, C, dwte, part);
+            hipLaunchKernelGGL(emb_combine_kernel, dim3((unsigned)nwin, (unsigned)cdiv(C / 4, 64)), dim3(64), 0, s,
+                               stok, bstart, nvalid, C, part, dwte);
         });
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -205,53 +205,58 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const uint16_t* __restrict_
     }
 }
 
-// out0[c] += sum_b partial[b][0][c], out1[c] += sum_b partial[b][1][c].  Block
-// (x, y) sums partial rows y, y + FOLD_SEGS, ... for 256 columns (coalesced
-// loads, 8 independent accumulators) and adds its segment sum atomically, so
-// the fold runs FOLD_SEGS-way parallel over the rows.
+// Fold of the per-block column partials into dw (rows [0, C)) and db (rows
+// [C, 2C)), in two launches whose additions happen in a fixed order, so the
+// parameter gradients are the same bits on every run.  Stage 1: block (x, y, z)
+// sums partial rows y, y + FOLD_SEGS, ... of slot z for 256 columns (coalesced
+// loads, 8 independent accumulators) and stores the segment sum in row y, the
+// first row it read (no other block reads those columns of that row).  Stage 2
+// adds the min(FOLD_SEGS, nblocks) segment sums of a column in segment order.
 constexpr int FOLD_SEGS = 16;
-__global__ __launch_bounds__(256) void fold_partials_kernel(const float* __restrict__ partial, int nblocks, int C,
-                                                            float* __restrict__ out0, float* __restrict__ out1) {
-    const int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= 2 * C) return;
-    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int b = blockIdx.y;
-    for (; b + 7 * FOLD_SEGS < nblocks; b += 8 * FOLD_SEGS) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) s[u] += partial[(int64_t)(b + u * FOLD_SEGS) * 2 * C + c];
-    }
-    for (; b < nblocks; b += FOLD_SEGS) s[0] += partial[(int64_t)b * 2 * C + c];
-    const float t = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
-    if (c < C)
-        unsafeAtomicAdd(out0 + c, t);
-    else
-        unsafeAtomicAdd(out1 + c - C, t);
-}
-
-// The same fold for several LayerNorms at once: z-slice z sums partial slot z
-// into dw[z], db[z].
 struct LnFoldSet {
     float* dw[LN_FOLD_MAX];
     float* db[LN_FOLD_MAX];
 };
-__global__ __launch_bounds__(256) void fold_partials_many_kernel(const float* __restrict__ partial, int64_t slot_elems,
-                                                                 int nblocks, int C, LnFoldSet set) {
-    const int z = blockIdx.z;
-    const float* part = partial + (int64_t)z * slot_elems;
+__global__ __launch_bounds__(256) void fold_segments_kernel(float* __restrict__ partial, int64_t slot_elems,
+                                                            int nblocks, int C) {
+    float* part = partial + (int64_t)blockIdx.z * slot_elems;
     const int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= 2 * C) return;
+    const int y = blockIdx.y;
+    if (c >= 2 * C || y >= nblocks) return;
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int b = blockIdx.y;
+    int b = y;
     for (; b + 7 * FOLD_SEGS < nblocks; b += 8 * FOLD_SEGS) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) s[u] += part[(int64_t)(b + u * FOLD_SEGS) * 2 * C + c];
     }
     for (; b < nblocks; b += FOLD_SEGS) s[0] += part[(int64_t)b * 2 * C + c];
-    const float t = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+    part[(int64_t)y * 2 * C + c] = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+}
+__global__ __launch_bounds__(256) void fold_finish_kernel(const float* __restrict__ partial, int64_t slot_elems,
+                                                          int nblocks, int C, LnFoldSet set) {
+    const float* part = partial + (int64_t)blockIdx.y * slot_elems;
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= 2 * C) return;
+    const int nseg = min(FOLD_SEGS, nblocks);
+    float t = 0.f;
+    for (int y = 0; y < nseg; ++y) t += part[(int64_t)y * 2 * C + c];
     if (c < C)
-        unsafeAtomicAdd(set.dw[z] + c, t);
+        set.dw[blockIdx.y][c] += t;
     else
-        unsafeAtomicAdd(set.db[z] + c - C, t);
+        set.db[blockIdx.y][c - C] += t;
+}
+
+hipError_t fold_slots(float* partial, int64_t slot_elems, int nslots, int nblocks, int C, const LnFoldSet& set,
+                      hipStream_t s) {
+    PROF_LAUNCH(KC_FOLD, 8.0 * nblocks * C * nslots, s,
+                hipLaunchKernelGGL(fold_segments_kernel, dim3(cdiv(2 * C, 256), FOLD_SEGS, nslots), dim3(256), 0, s,
+                                   partial, slot_elems, nblocks, C));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    PROF_LAUNCH(KC_FOLD, 8.0 * std::min(FOLD_SEGS, nblocks) * C * nslots, s,
+                hipLaunchKernelGGL(fold_finish_kernel, dim3(cdiv(2 * C, 256), nslots), dim3(256), 0, s, partial,
+                                   slot_elems, nblocks, C, set));
+    return hipGetLastError();
 }
 
 int ln_blocks(int64_t rows) { return (int)std::min<int64_t>(768, cdiv(rows, ROWS_PER_BLOCK)); }
@@ -277,10 +282,10 @@ hipError_t ln_bwd_t(const uint16_t* x, const uint16_t* dy, const float* w, const
                        accumulate, partial, rows));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || dw == nullptr) return e;  // no dw: the partials are folded later
-    PROF_LAUNCH(KC_FOLD, 8.0 * blocks * C, s,
-                hipLaunchKernelGGL(fold_partials_kernel, dim3(cdiv(2 * C, 256), FOLD_SEGS), dim3(256), 0, s, partial,
-                                   blocks, C, dw, db));
-    return hipGetLastError();
+    LnFoldSet set{};
+    set.dw[0] = dw;
+    set.db[0] = db;
+    return fold_slots(partial, (int64_t)blocks * 2 * C, 1, blocks, C, set, s);
 }
 
 }  // namespace
@@ -324,19 +329,15 @@ hipError_t launch_layernorm_bwd(const uint16_t* x, const uint16_t* dy, const flo
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_layernorm_fold(const float* partial, int64_t slot_elems, int nslots, float* const* dw,
-                                 float* const* db, int64_t rows, int C, hipStream_t s) {
+hipError_t launch_layernorm_fold(float* partial, int64_t slot_elems, int nslots, float* const* dw, float* const* db,
+                                 int64_t rows, int C, hipStream_t s) {
     if (nslots < 1 || nslots > LN_FOLD_MAX || rows <= 0) return nslots == 0 ? hipSuccess : hipErrorInvalidValue;
     LnFoldSet set{};
     for (int i = 0; i < nslots; ++i) {
         set.dw[i] = dw[i];
         set.db[i] = db[i];
     }
-    const int blocks = ln_blocks(rows);
-    PROF_LAUNCH(KC_FOLD, 8.0 * blocks * C * nslots, s,
-                hipLaunchKernelGGL(fold_partials_many_kernel, dim3(cdiv(2 * C, 256), FOLD_SEGS, nslots), dim3(256), 0,
-                                   s, partial, slot_elems, blocks, C, set));
-    return hipGetLastError();
+    return fold_slots(partial, slot_elems, nslots, ln_blocks(rows), C, set, s);
 }
 
 bool layernorm_supports(int C) {

@@ -50,9 +50,10 @@ hipError_t launch_layernorm_fwd(const uint16_t* x, const float* w, const float* 
 int64_t layernorm_bwd_partial_elems(int64_t rows, int C);
 // With dw == nullptr the LayerNorm backward leaves its column partials in
 // `partial` (layernorm_bwd_partial_elems floats); launch_layernorm_fold then
-// adds slots 0..nslots-1 (slot_elems apart) into dw[i], db[i] in one launch.
+// adds slots 0..nslots-1 (slot_elems apart) into dw[i], db[i] (two launches, a
+// fixed order of additions; the slots are overwritten).
 constexpr int LN_FOLD_MAX = 64;
-hipError_t launch_layernorm_fold(const float* partial, int64_t slot_elems, int nslots, float* const* dw,
+hipError_t launch_layernorm_fold(float* partial, int64_t slot_elems, int nslots, float* const* dw,
                                  float* const* db, int64_t rows, int C, hipStream_t s);
 // dres = (accumulate ? dres_in : 0) + dx; dres_in may equal dres (in place)
 hipError_t launch_layernorm_bwd(const uint16_t* x, const uint16_t* dy, const float* w, const float* mean,
@@ -71,8 +72,9 @@ hipError_t launch_xent(uint16_t* logits, const int32_t* tgt, float* loss_rows, i
 hipError_t launch_mean(const float* x, const int32_t* tgt, int64_t n, float* out, hipStream_t s);
 hipError_t launch_embedding_fwd(const int32_t* tok, const uint16_t* wte, const uint16_t* wpe, uint16_t* x, int B,
                                 int T, int C, int V, int32_t* flag, hipStream_t s);
-// work: embedding_bwd_work_elems(B*T, V) int32 scratch (counting sort of the rows by token)
-int64_t embedding_bwd_work_elems(int64_t rows, int V);
+// work: embedding_bwd_work_elems(B*T, V, C) int32 scratch, 16-byte aligned (counting sort of
+// the rows by token, bucket starts, and the pieces of runs that cross summation windows)
+int64_t embedding_bwd_work_elems(int64_t rows, int V, int C);
 hipError_t launch_embedding_bwd(const int32_t* tok, const uint16_t* dx, float* dwte, float* dwpe, int B, int T,
                                 int C, int V, int32_t* work, int64_t work_elems, hipStream_t s);
 

@@ -420,6 +420,6 @@ def embedding_fwd(tok, wte, wpe, V, flag=None):
 def embedding_bwd(tok, dx, dwte, dwpe, V):
     B, T = tok.shape
     C = dx.shape[1]
-    s = _scratch(scratch_bytes(5, B * T, V), dx.device)
+    s = _scratch(scratch_bytes(5, B * T, V, C), dx.device)
     check(load().gpt2k_embedding_bwd(_ptr(tok), _ptr(dx), _ptr(dwte), _ptr(dwpe), B, T, C, V, _ptr(s), s.numel(),
                                      _stream()), "gpt2k_embedding_bwd")
