@@ -628,6 +628,9 @@ struct TnGroup {
     TnJob job[TN_MAX_JOBS];
     int tile_start[TN_MAX_JOBS + 1];  // prefix sums of the jobs' tile counts
     int njobs, splits, nk_total;      // nk_total = tokens / 64
+    // split launches (EPI_F32_STORE): split s of job j leaves its bias column sums at
+    // bpart + splits * (M_0 + ... + M_{j-1}) + s * M_j, added in split order by the reduce
+    float* bpart;
 };
 
 template <int EPI, int NS, int TD>
@@ -767,7 +770,16 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(TnGroup G) {
         for (int i = 0; i < 4; ++i) {
             const float t = bsum[i] + __shfl_xor(bsum[i], 32, WAVE);
             const int row = m0 + wm * 128 + i * 32 + (lane & 31);
-            if (g == 0 && row < p.M) unsafeAtomicAdd(p.dbias + row, t);
+            if constexpr (EPI == EPI_F32_STORE) {
+                // several splits per row: each leaves its sum for the ordered reduce
+                if (g == 0 && row < p.M) {
+                    int64_t off = 0;
+                    for (int j = 0; j < jb; ++j) off += G.job[j].M;
+                    G.bpart[off * G.splits + (int64_t)split * p.M + row] = t;
+                }
+            } else {
+                if (g == 0 && row < p.M) unsafeAtomicAdd(p.dbias + row, t);  // one writer per row
+            }
         }
     }
 
@@ -825,9 +837,15 @@ __global__ void splitk_reduce_kernel(const float4* __restrict__ part, float4* __
 struct TnReduce {
     const float4* part[TN_MAX_JOBS];
     float4* dw[TN_MAX_JOBS];
+    const float* bpart[TN_MAX_JOBS];
+    float* db[TN_MAX_JOBS];
     int64_t start4[TN_MAX_JOBS + 1];
+    int bstart[TN_MAX_JOBS + 1];
     int njobs, splits;
 };
+// dW_j += the splits' partials of job j (float4 vectors [start4[j], start4[j+1]) of
+// one index space) and db_j += the splits' bias column sums (rows [bstart[j],
+// bstart[j+1]) of a second one), all jobs of a group in one launch, splits in order.
 __global__ void splitk_reduce_group_kernel(TnReduce R) {
     const int64_t n4 = R.start4[R.njobs];
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
@@ -840,6 +858,16 @@ __global__ void splitk_reduce_group_kernel(TnReduce R) {
             a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
         }
         R.dw[j][e] = a;
+    }
+    const int nb = R.bstart[R.njobs];
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nb; i += gridDim.x * blockDim.x) {
+        int j = 0;
+        while (j + 1 < R.njobs && i >= R.bstart[j + 1]) ++j;
+        if (R.db[j] == nullptr) continue;
+        const int r = i - R.bstart[j], rows = R.bstart[j + 1] - R.bstart[j];
+        float a = R.db[j][r];
+        for (int sp = 0; sp < R.splits; ++sp) a += R.bpart[j][(int64_t)sp * rows + r];
+        R.db[j][r] = a;
     }
 }
 
@@ -963,15 +991,15 @@ bool tn_tail_plan(int N, int K, int nk, int* full_rows, int* tail_splits) {
     return true;
 }
 
-// Column-sum partials for the bias gradients of a split launch (one product at a time).
-int64_t tn_bias_partial_elems(const TnJobDesc* jobs, int n, int M) {
+// Bias column sums of a split launch: one row per output row of each product and split.
+int64_t tn_bias_partial_elems(const TnJobDesc* jobs, int n, int splits) {
     int64_t e = 0;
-    for (int j = 0; j < n; ++j) e = std::max(e, colsum_partial_elems(M, jobs[j].N));
+    for (int j = 0; j < n; ++j) e += (int64_t)splits * jobs[j].N;
     return e;
 }
 
 // Runs jobs [0, n) of equal token count M as one grouped 256x256-tile launch
-// (plus one reduce launch, and the bias column sums, when split).
+// (plus one reduce launch when split).
 hipError_t run_tn_group(const TnJobDesc* jobs, int n, int M, float* partial, int64_t partial_elems, hipStream_t s) {
     TnGroup G{};
     G.njobs = n;
@@ -991,7 +1019,7 @@ hipError_t run_tn_group(const TnJobDesc* jobs, int n, int M, float* partial, int
     }
     G.tile_start[n] = (int)tiles;
     int sp = tn_group_splits(tiles, G.nk_total);
-    if (sp > 1 && (partial == nullptr || partial_elems < sp * elems + tn_bias_partial_elems(jobs, n, M))) sp = 1;
+    if (sp > 1 && (partial == nullptr || partial_elems < sp * elems + tn_bias_partial_elems(jobs, n, sp))) sp = 1;
     G.splits = sp;
     if (sp == 1) {
         for (int j = 0; j < n; ++j) G.job[j].out = jobs[j].dW;
@@ -1007,27 +1035,28 @@ hipError_t run_tn_group(const TnJobDesc* jobs, int n, int M, float* partial, int
     for (int j = 0; j < n; ++j) {
         const int64_t e = (int64_t)jobs[j].N * jobs[j].K;
         G.job[j].out = partial + off;
-        // the splits of a product would add into each bias row in no fixed order:
-        // its bias gradient is summed afterwards by the column-sum kernel instead
-        G.job[j].dbias = nullptr;
         R.part[j] = (const float4*)(partial + off);
         R.dw[j] = (float4*)jobs[j].dW;
         R.start4[j + 1] = R.start4[j] + e / 4;
         off += sp * e;
+    }
+    G.bpart = partial + off;  // then the splits' bias column sums, sp * N floats per job
+    for (int j = 0; j < n; ++j) {
+        R.bpart[j] = partial + off;
+        R.db[j] = jobs[j].db;
+        R.bstart[j + 1] = R.bstart[j] + jobs[j].N;
+        off += (int64_t)sp * jobs[j].N;
     }
     PROF_LAUNCH(KC_GEMM_TN_SPLIT, work, s,
                 hipLaunchKernelGGL((gemm_tn_w8_kernel<EPI_F32_STORE, TN_STAGES, TN_TD>), dim3(tiles * sp),
                                    dim3(512), 0, s, G));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t n4 = R.start4[n];
+    const int64_t n4 = std::max<int64_t>(R.start4[n], R.bstart[n]);
     const int blocks = (int)std::min<int64_t>(cdiv(n4, 256), 4096);
     PROF_LAUNCH(KC_SPLITK_REDUCE, 16.0 * n4 * (sp + 2), s,
                 hipLaunchKernelGGL(splitk_reduce_group_kernel, dim3(blocks), dim3(256), 0, s, R));
-    e = hipGetLastError();
-    for (int j = 0; j < n && e == hipSuccess; ++j)
-        if (jobs[j].db != nullptr) e = launch_bias_grad(jobs[j].dY, jobs[j].ldy, jobs[j].db, partial + off, M, jobs[j].N, s);
-    return e;
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -1108,20 +1137,16 @@ hipError_t launch_gemm_tn_group(const TnJobDesc* jobs, int n, int M, float* part
     return hipSuccess;
 }
 
-// Split partials of a launch (splits x N x K per product) plus the column-sum
-// partials of its bias gradients.
+// Split partials of a launch: splits x (N x K dW partials + N bias column sums) per product.
 int64_t gemm_tn_group_partial_elems(const TnJobDesc* jobs, int n, int M) {
     int full_rows = 0, tail_sp = 1;
     if (n == 1 && tn_tail_plan(jobs[0].N, jobs[0].K, M / BK, &full_rows, &tail_sp))
-        return (int64_t)tail_sp * (jobs[0].N - full_rows) * jobs[0].K + colsum_partial_elems(M, jobs[0].N - full_rows);
+        return (int64_t)tail_sp * (jobs[0].N - full_rows) * (jobs[0].K + 1);
     int hi[TN_MAX_JOBS], ti[TN_MAX_JOBS], nh = 0, nt = 0;
     if (n <= TN_MAX_JOBS && tn_group_tail_plan(jobs, n, M / BK, hi, &nh, ti, &nt, &tail_sp)) {
-        int64_t e = 0, b = 0;
-        for (int i = 0; i < nt; ++i) {
-            e += (int64_t)jobs[ti[i]].N * jobs[ti[i]].K;
-            b = std::max(b, colsum_partial_elems(M, jobs[ti[i]].N));
-        }
-        return tail_sp * e + b;
+        int64_t e = 0;
+        for (int i = 0; i < nt; ++i) e += (int64_t)jobs[ti[i]].N * (jobs[ti[i]].K + 1);
+        return tail_sp * e;
     }
     int64_t tiles = 0, elems = 0;
     for (int j = 0; j < n; ++j) {
@@ -1129,5 +1154,5 @@ int64_t gemm_tn_group_partial_elems(const TnJobDesc* jobs, int n, int M) {
         elems += (int64_t)jobs[j].N * jobs[j].K;
     }
     const int sp = tn_group_splits(tiles, M / BK);
-    return sp > 1 ? sp * elems + tn_bias_partial_elems(jobs, n, M) : 0;
+    return sp > 1 ? sp * elems + tn_bias_partial_elems(jobs, n, sp) : 0;
 }
