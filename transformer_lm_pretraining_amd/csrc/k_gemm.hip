@@ -675,20 +675,24 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(TnGroup G) {
         offB[i] = (uint32_t)(tok0 + row) * (uint32_t)p.ldb + (uint32_t)min(n0 + lv * 8, p.N - 8);
     }
     const uint32_t stepA = (uint32_t)TD * (uint32_t)p.lda, stepB = (uint32_t)TD * (uint32_t)p.ldb;
+    // Every stage boundary issues one group of loads, so the number in flight is the
+    // same at every wait (one immediate s_waitcnt, no run-time switch): stage t goes
+    // to buffer t % NS, and past the last stage the last stage's data is loaded
+    // again into the buffer just released, which is never read.
     auto issue = [&](int t) {
         uint16_t* sa = smem + (t % NS) * SE;
         uint16_t* sb = sa + TD * BIG;
+        const uint32_t ts = (uint32_t)min(t, nk - 1);
 #pragma unroll
         for (int i = 0; i < IPO; ++i)
-            lds_dma16_asm(p.A + (offA[i] + (uint32_t)t * stepA), sa + 2 * (wave * IPO + i) * BIG);
+            lds_dma16_asm(p.A + (offA[i] + ts * stepA), sa + 2 * (wave * IPO + i) * BIG);
 #pragma unroll
         for (int i = 0; i < IPO; ++i)
-            lds_dma16_asm(p.B + (offB[i] + (uint32_t)t * stepB), sb + 2 * (wave * IPO + i) * BIG);
+            lds_dma16_asm(p.B + (offB[i] + ts * stepB), sb + 2 * (wave * IPO + i) * BIG);
     };
 
 #pragma unroll
-    for (int t = 0; t < NS; ++t)
-        if (t < nk) issue(t);
+    for (int t = 0; t < NS; ++t) issue(t);
     __builtin_amdgcn_sched_barrier(0);
 
     // acc[i][j][4*rg + e] is dW[m0 + wm*128 + i*32 + (lane&31)][n0 + wn*64 + j*32 + 8*rg + 4*g + e]
@@ -700,7 +704,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(TnGroup G) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     float bsum[4] = {0.f, 0.f, 0.f, 0.f};
-    wait_stage_groups<2 * IPO>(min(NS, nk) - 1);
+    __builtin_amdgcn_s_waitcnt(vm_imm((NS - 1) * 2 * IPO));  // stage 0 has landed
     __syncthreads();
 
     // per-lane fragment addresses within a stage tile (token row 4g + (lane&15)/4,
@@ -749,10 +753,11 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(TnGroup G) {
             if (kk + 1 < KS) {
                 read_frags(st, kk + 1, b ^ 1);
             } else if (s + 1 < nk) {
-                wait_stage_groups<2 * IPO>(min(s + NS - 1, nk - 1) - (s + 1));
+                // stage s+1 has landed once only the NS-2 groups issued after it remain
+                __builtin_amdgcn_s_waitcnt(vm_imm((NS - 2) * 2 * IPO));
                 __syncthreads();
                 // all of stage s is in registers: its buffer takes stage s+NS
-                if (s + NS < nk) issue(s + NS);
+                issue(s + NS);
                 read_frags(smem + ((s + 1) % NS) * SE, 0, b ^ 1);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -761,6 +766,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(TnGroup G) {
             __builtin_amdgcn_sched_barrier(0);
         }
     } while (++s < nk);
+    __builtin_amdgcn_s_waitcnt(vm_imm(0));  // the loads past the last stage have landed before the LDS is reused
     __syncthreads();
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
