@@ -110,7 +110,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     const int nqb = (int)(gridDim.x / (unsigned)BH);
     const int q0 = (nqb - 1 - attn_unit(BH, bh)) * QB;  // heaviest blocks first
     const int b = bh / H, h = bh % H;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: causal tests are scalar branches
     const int64_t ld = 3 * (int64_t)C;
     const uint16_t* Qg = qkv + (int64_t)b * T * ld + h * D;
     const uint16_t* Kg = Qg + C;
@@ -281,7 +282,8 @@ __global__ __launch_bounds__(256, 2) void attn_dkdv_kernel(const uint16_t* __res
     int bh;
     const int k0 = attn_unit(BH, bh) * QB;  // the first key blocks see the most queries
     const int b = bh / H, h = bh % H;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: causal tests are scalar branches
     const int64_t ld = 3 * (int64_t)C;
     const uint16_t* Qg = qkv + (int64_t)b * T * ld + h * D;
     const uint16_t* Kg = Qg + C;
@@ -445,7 +447,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const uint16_t* __restr
     const int nqb = (int)(gridDim.x / (unsigned)BH);
     const int q0 = (nqb - 1 - attn_unit(BH, bh)) * QB;
     const int b = bh / H, h = bh % H;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: causal tests are scalar branches
     const int64_t ld = 3 * (int64_t)C;
     const uint16_t* Qg = qkv + (int64_t)b * T * ld + h * D;
     const uint16_t* Kg = Qg + C;
