@@ -20,6 +20,7 @@
 // a second kernel.
 #include <algorithm>
 #include "common.h"
+#include <type_traits>
 #include "kernels.h"
 #include "prof.h"
 
@@ -661,7 +662,10 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(TnGroup G) {
     const int q = steps / G.splits, rr = steps % G.splits;
     const int nk = q + (split < rr ? 1 : 0);                 // >= 1: the host keeps splits <= steps
     const int tok0 = (split * q + min(split, rr)) * TD;
-    const bool sum_rows = p.dbias != nullptr && tn == 0 && wn == 0;
+    // bias column sums: in the tiles of the first X column block, the four waves of a
+    // wave row read the same dY fragments; wave wn sums fragment group i = wn
+    const bool sum_rows = p.dbias != nullptr && tn == 0;
+    const int bw = __builtin_amdgcn_readfirstlane(wn);
 
     // Load instruction i of this wave covers token rows 2*(wave*IPO + i) + (lane>>5)
     // of the stage, physical vector lane&31, i.e. logical vector (lane&31) ^ ((row&7)<<2).
@@ -703,7 +707,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(TnGroup G) {
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    float bsum[4] = {0.f, 0.f, 0.f, 0.f};
+    float bsum = 0.f;
     __builtin_amdgcn_s_waitcnt(vm_imm((NS - 1) * 2 * IPO));  // stage 0 has landed
     __syncthreads();
 
@@ -726,12 +730,12 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(TnGroup G) {
         for (int j = 0; j < 2; ++j) xf[b][j] = tn_frag(st + fb[j] + ks * 16 * BIG);
     };
     auto add_bias = [&](int b) {
-        if (sum_rows) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i) {
+            if (bw == i) {
                 const u32x4 w = __builtin_bit_cast(u32x4, dyf[b][i]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) bsum[i] += bflo(w[e]) + bfhi(w[e]);
+                for (int e = 0; e < 4; ++e) bsum += bflo(w[e]) + bfhi(w[e]);
             }
         }
     };
@@ -741,41 +745,47 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(TnGroup G) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(xf[b][j], dyf[b][i], acc[i][j]);
     };
-    read_frags(smem, 0, 0);
-    int s = 0;
-    do {
-        const uint16_t* st = smem + (s % NS) * SE;
+    // two copies of the main loop: tiles without bias sums carry no bias code at all
+    auto main_loop = [&](auto with_bias) {
+        read_frags(smem, 0, 0);
+        int s = 0;
+        do {
+            const uint16_t* st = smem + (s % NS) * SE;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            const int b = kk & 1;
-            mma(b, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            if (kk + 1 < KS) {
-                read_frags(st, kk + 1, b ^ 1);
-            } else if (s + 1 < nk) {
-                // stage s+1 has landed once only the NS-2 groups issued after it remain
-                __builtin_amdgcn_s_waitcnt(vm_imm((NS - 2) * 2 * IPO));
-                __syncthreads();
-                // all of stage s is in registers: its buffer takes stage s+NS
-                issue(s + NS);
-                read_frags(smem + ((s + 1) % NS) * SE, 0, b ^ 1);
+            for (int kk = 0; kk < KS; ++kk) {
+                const int b = kk & 1;
+                mma(b, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (kk + 1 < KS) {
+                    read_frags(st, kk + 1, b ^ 1);
+                } else if (s + 1 < nk) {
+                    // stage s+1 has landed once only the NS-2 groups issued after it remain
+                    __builtin_amdgcn_s_waitcnt(vm_imm((NS - 2) * 2 * IPO));
+                    __syncthreads();
+                    // all of stage s is in registers: its buffer takes stage s+NS
+                    issue(s + NS);
+                    read_frags(smem + ((s + 1) % NS) * SE, 0, b ^ 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                mma(b, 2);
+                if constexpr (decltype(with_bias)::value) add_bias(b);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            mma(b, 2);
-            add_bias(b);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    } while (++s < nk);
+        } while (++s < nk);
+    };
+    if (sum_rows)
+        main_loop(std::true_type{});
+    else
+        main_loop(std::false_type{});
     __builtin_amdgcn_s_waitcnt(vm_imm(0));  // the loads past the last stage have landed before the LDS is reused
     __syncthreads();
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
     if (sum_rows) {
         // the two lane halves hold different tokens of the same feature rows
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float t = bsum[i] + __shfl_xor(bsum[i], 32, WAVE);
-            const int row = m0 + wm * 128 + i * 32 + (lane & 31);
+        {
+            const float t = bsum + __shfl_xor(bsum, 32, WAVE);
+            const int row = m0 + wm * 128 + bw * 32 + (lane & 31);
             if constexpr (EPI == EPI_F32_STORE) {
                 // several splits per row: each leaves its sum for the ordered reduce
                 if (g == 0 && row < p.M) {
