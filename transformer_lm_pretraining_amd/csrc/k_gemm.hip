@@ -729,15 +729,10 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(TnGroup G) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) xf[b][j] = tn_frag(st + fb[j] + ks * 16 * BIG);
     };
-    auto add_bias = [&](int b) {
+    auto add_bias = [&](int b, auto fi) {
+        const u32x4 w = __builtin_bit_cast(u32x4, dyf[b][decltype(fi)::value]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (bw == i) {
-                const u32x4 w = __builtin_bit_cast(u32x4, dyf[b][i]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) bsum += bflo(w[e]) + bfhi(w[e]);
-            }
-        }
+        for (int e = 0; e < 4; ++e) bsum += bflo(w[e]) + bfhi(w[e]);
     };
     auto mma = [&](int b, int i0) {
 #pragma unroll
@@ -746,7 +741,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(TnGroup G) {
             for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(xf[b][j], dyf[b][i], acc[i][j]);
     };
     // two copies of the main loop: tiles without bias sums carry no bias code at all
-    auto main_loop = [&](auto with_bias) {
+    auto main_loop = [&](auto bias_frag) {
         read_frags(smem, 0, 0);
         int s = 0;
         do {
@@ -768,15 +763,21 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(TnGroup G) {
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 mma(b, 2);
-                if constexpr (decltype(with_bias)::value) add_bias(b);
+                if constexpr (decltype(bias_frag)::value >= 0) add_bias(b, bias_frag);
                 __builtin_amdgcn_sched_barrier(0);
             }
         } while (++s < nk);
     };
-    if (sum_rows)
-        main_loop(std::true_type{});
+    if (!sum_rows)
+        main_loop(std::integral_constant<int, -1>{});
+    else if (bw == 0)
+        main_loop(std::integral_constant<int, 0>{});
+    else if (bw == 1)
+        main_loop(std::integral_constant<int, 1>{});
+    else if (bw == 2)
+        main_loop(std::integral_constant<int, 2>{});
     else
-        main_loop(std::false_type{});
+        main_loop(std::integral_constant<int, 3>{});
     __builtin_amdgcn_s_waitcnt(vm_imm(0));  // the loads past the last stage have landed before the LDS is reused
     __syncthreads();
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
