@@ -9,6 +9,10 @@
  * row-major arrays, 256-byte aligned device pointers, status codes
  * GPT2_OK / GPT2_E_*.  Sources are cited as in gpt2mi.h (PDS, GLM =
  * "Was ein Sprachmodell vorhersagt", activity table).
+ * Empty inputs: the row-wise calls (xent, layernorm_*, bias_gelu_*, bias_grad)
+ * accept rows == 0 and then launch nothing, write nothing and return GPT2_OK;
+ * the GEMM, attention and embedding calls need at least one row (B, T, M >= 1)
+ * and return GPT2_E_INVALID otherwise, before any device work.
  */
 #ifndef GPT2MI_KERNELS_H
 #define GPT2MI_KERNELS_H

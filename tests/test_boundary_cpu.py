@@ -102,6 +102,12 @@ def test_kernel_entry_points_validate_before_launch(L):
     assert L.gpt2k_attention_fwd(256, 256, 256, 1, 100, 2, 128, None) == lib.GPT2_E_INVALID
     assert L.gpt2k_attention_fwd(256, 256, 256, 1, 64, 1, 128, None) == lib.GPT2_E_SHAPE
     assert L.gpt2k_layernorm_fwd(256, 256, 256, 256, 256, 256, 4, 100, None) == lib.GPT2_E_SHAPE
+    # sizes below a call's minimum are refused, not launched as empty grids
+    assert L.gpt2k_gemm_nt(256, 256, None, None, 256, 0, 64, 64, None) == lib.GPT2_E_INVALID
+    assert L.gpt2k_gemm_tn_acc(256, 256, 256, None, 256, 1 << 20, 0, 64, 64, None) == lib.GPT2_E_INVALID
+    assert L.gpt2k_attention_fwd(256, 256, 256, 0, 64, 2, 128, None) == lib.GPT2_E_INVALID
+    assert L.gpt2k_embedding_fwd(256, 256, 256, 256, 0, 64, 128, 100, None, None) == lib.GPT2_E_INVALID
+    assert L.gpt2k_embedding_bwd(256, 256, 256, 256, 1, 0, 128, 100, 256, 1 << 20, None) == lib.GPT2_E_INVALID
     out = ctypes.c_int64()
     assert L.gpt2k_scratch_bytes(1, 19456, 768, 0, ctypes.byref(out)) == 0 and out.value > 0
     assert L.gpt2k_scratch_bytes(9, 1, 1, 1, ctypes.byref(out)) == lib.GPT2_E_INVALID
