@@ -65,6 +65,14 @@ struct GemmParams {
 // band = 0 the sequence is dealt round-robin (split into 8 contiguous shares
 // when ntiles is a multiple of 8) over bands of GROUP_M row tiles; for outputs
 // a few tiles wide that keeps every column tile of a row tile on one XCD.
+// Workgroup ids go round-robin over the XCDs.  Renumbered so that each XCD holds
+// one contiguous run of tiles (XCD x takes total/8 ids, one more when x < total % 8),
+// tiles that share operand slices meet in that XCD's L2 at any tile count.
+__device__ __forceinline__ int xcd_contiguous(int lin, int total) {
+    const int q = total / NUM_XCD, r = total % NUM_XCD, x = lin % NUM_XCD;
+    return x * q + min(x, r) + lin / NUM_XCD;
+}
+
 __device__ __forceinline__ void nt_tile(int lin, int tiles_m, int tiles_n, int band, int& tm, int& tn) {
     const int ntiles = tiles_m * tiles_n;
     int pid;
@@ -645,8 +653,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(TnGroup G) {
 
     const int ntiles = G.tile_start[G.njobs];
     const int total = ntiles * G.splits;
-    int lin = blockIdx.x;
-    if ((total % NUM_XCD) == 0) lin = (lin % NUM_XCD) * (total / NUM_XCD) + lin / NUM_XCD;
+    const int lin = xcd_contiguous(blockIdx.x, total);
     const int split = lin / ntiles;
     int pid = lin % ntiles, jb = 0;
     while (jb + 1 < G.njobs && pid >= G.tile_start[jb + 1]) ++jb;
