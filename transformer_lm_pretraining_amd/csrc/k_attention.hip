@@ -237,29 +237,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
 
 // ---------------------------------------------------------------- backward
 
-// dvec[b,h,i] = sum_d dO[i, h*D + d] * O[i, h*D + d]
-template <int D>
-__global__ __launch_bounds__(256) void attn_dvec_kernel(const uint16_t* __restrict__ out,
-                                                        const uint16_t* __restrict__ dout, float* __restrict__ dvec,
-                                                        int B, int T, int H, int C) {
-    const int64_t n = (int64_t)B * T * H;
-    for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t row = idx / H;
-        const int h = (int)(idx % H);
-        const u32x4* o = (const u32x4*)(out + row * C + h * D);
-        const u32x4* d = (const u32x4*)(dout + row * C + h * D);
-        float s = 0.f;
-#pragma unroll
-        for (int v = 0; v < D / 8; ++v) {
-            u32x4 a = o[v], c = d[v];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s += bflo(a[e]) * bflo(c[e]) + bfhi(a[e]) * bfhi(c[e]);
-        }
-        const int64_t b = row / T, t = row % T;
-        dvec[(b * H + h) * T + t] = s;
-    }
-}
-
 // dK, dV for 128 keys per workgroup (lane = key), looping over 64-query blocks;
 // each block is processed as two 32-query halves (it).  Per half: Q and dO
 // fragments -> S and dP MFMAs; Q^T and dO^T fragments are read while the
@@ -434,9 +411,10 @@ __global__ __launch_bounds__(256, 2) void attn_dkdv_kernel(const uint16_t* __res
 // dS^T = P^T (dP^T - D) is formed; then dQ^T += K^T dS^T.
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const uint16_t* __restrict__ qkv,
+                                                         const uint16_t* __restrict__ out,
                                                          const uint16_t* __restrict__ dout,
                                                          const float* __restrict__ lse,
-                                                         const float* __restrict__ dvec,
+                                                         float* __restrict__ dvec,
                                                          uint16_t* __restrict__ dqkv, int T, int H, int C,
                                                          int BH, float sl, float scale) {
     constexpr int LD = D + 8;
@@ -465,7 +443,14 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const uint16_t* __restr
         df[kk] = qvalid ? *(const bf16x8*)(dOg + (int64_t)qi * C + kk * 16 + g * 8) : bf16x8{};
     }
     const float lse2 = qvalid ? lse[((int64_t)b * H + h) * T + qi] * LOG2E : 0.f;
-    const float dvi = qvalid ? dvec[((int64_t)b * H + h) * T + qi] : 0.f;
+    // D = rowsum(dO * O) of this lane's query: the lane pair (g = 0, 1) holds
+    // complementary halves of the dO row, the matching O halves are read with it.
+    // The sum is taken once the first K/V block's loads are in flight; the dK/dV
+    // kernel, launched after this one, reads D from dvec.
+    bf16x8 of[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+        of[kk] = qvalid ? *(const bf16x8*)(out + ((int64_t)b * T + qi) * C + h * D + kk * 16 + g * 8) : bf16x8{};
     floatx16 acc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -478,6 +463,16 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const uint16_t* __restr
     Stage<D> stk, stv;
     stk.load(Kg, ld, 0, tid);
     stv.load(Vg, ld, 0, tid);
+    float dvi = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        const u32x4 o = __builtin_bit_cast(u32x4, of[kk]);
+        const u32x4 d = __builtin_bit_cast(u32x4, df[kk]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dvi += bflo(o[e]) * bflo(d[e]) + bfhi(o[e]) * bfhi(d[e]);
+    }
+    dvi += __shfl_xor(dvi, 32, WAVE);
+    if (qvalid && g == 0) dvec[((int64_t)b * H + h) * T + qi] = dvi;
     stk.store(sK[0], tid);
     stv.store(sV[0], tid);
     __syncthreads();
@@ -576,20 +571,14 @@ hipError_t bwd_t(const uint16_t* qkv, const uint16_t* out, const uint16_t* dout,
                  float* dvec, int B, int T, int H, int C, hipStream_t s) {
     const float scale = 1.0f / sqrtf((float)D);
     const float scale_log2 = LOG2E * scale;
-    int64_t n = (int64_t)B * T * H;
-    PROF_LAUNCH(KC_ATTN_DVEC, 4.0 * (double)n * D, s,
-                hipLaunchKernelGGL(attn_dvec_kernel<D>, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 8192)),
-                                   dim3(256), 0, s, out, dout, dvec, B, T, H, C));
+    dim3 grid((unsigned)(cdiv(T, QB) * B * H));
+    PROF_LAUNCH(KC_ATTN_DQ, attn_work(B, T, H, D, 3), s,
+                hipLaunchKernelGGL(attn_dq_kernel<D>, grid, dim3(256), 0, s, qkv, out, dout, lse, dvec, dqkv, T, H, C,
+                                   B * H, scale_log2, scale));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid((unsigned)(cdiv(T, QB) * B * H));
     PROF_LAUNCH(KC_ATTN_DKDV, attn_work(B, T, H, D, 4), s,
                 hipLaunchKernelGGL(attn_dkdv_kernel<D>, grid, dim3(256), 0, s, qkv, dout, lse, dvec, dqkv, T, H, C,
-                                   B * H, scale_log2, scale));
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    PROF_LAUNCH(KC_ATTN_DQ, attn_work(B, T, H, D, 3), s,
-                hipLaunchKernelGGL(attn_dq_kernel<D>, grid, dim3(256), 0, s, qkv, dout, lse, dvec, dqkv, T, H, C,
                                    B * H, scale_log2, scale));
     return hipGetLastError();
 }

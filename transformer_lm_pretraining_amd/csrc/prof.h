@@ -30,7 +30,7 @@ enum KernelClass {
     KC_GEMM_TN_SPLIT = 4,  // gemm_kernel TN, fp32 split-K partials
     KC_SPLITK_REDUCE = 5,
     KC_ATTN_FWD = 6,
-    KC_ATTN_DVEC = 7,
+    KC_ATTN_DVEC = 7,      // reserved: D = rowsum(dO * O) is taken inside the dQ kernel
     KC_ATTN_DKDV = 8,
     KC_ATTN_DQ = 9,
     KC_XENT = 10,
