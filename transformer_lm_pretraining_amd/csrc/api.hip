@@ -433,11 +433,18 @@ int run_backward(gpt2_handle* h, hipStream_t s) {
 }
 
 int refresh_shadow(gpt2_handle* h, hipStream_t s) {
-    // bf16 transposed copies of wte and the four matrices per block
+    // bf16 transposed copies of wte and the four matrices per block, one batched launch
+    std::vector<const uint16_t*> src;
+    std::vector<uint16_t*> dst;
+    std::vector<int> rows, cols;
     for (const Tensor& t : h->tens) {
         if (t.toff < 0) continue;
-        HIPCHK(launch_transpose_bf16(h->bufs.shadow + t.off, h->bufs.shadow_t + t.toff, (int)t.rows, (int)t.cols, s));
+        src.push_back(h->bufs.shadow + t.off);
+        dst.push_back(h->bufs.shadow_t + t.toff);
+        rows.push_back((int)t.rows);
+        cols.push_back((int)t.cols);
     }
+    HIPCHK(launch_transpose_bf16_batch(src.data(), dst.data(), rows.data(), cols.data(), (int)src.size(), s));
     return GPT2_OK;
 }
 

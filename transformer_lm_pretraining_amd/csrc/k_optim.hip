@@ -3,6 +3,7 @@
 // only, clipping to global norm 1.0; §4 precision: fp32 master weights,
 // gradients and optimizer state), plus the seeded init and bf16 shadow
 // maintenance.  All HBM-bound: float4 vectors, grid-stride loops.
+#include <algorithm>
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
@@ -123,6 +124,51 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
     }
 }
 
+// Several transposes in one launch, 64x64 tiles through LDS in 16-byte vectors:
+// dst_j[c][r] = src_j[r][c] for every job j (R_j and C_j multiples of 8).  Thread t
+// reads 8 consecutive columns of rows t/8 and t/8 + 32 and, after the barrier,
+// writes 8 consecutive rows of columns t/8 and t/8 + 32 of the transposed tile.
+constexpr int TR_MAX_JOBS = 64;
+struct TransposeJobs {
+    const uint16_t* src[TR_MAX_JOBS];
+    uint16_t* dst[TR_MAX_JOBS];
+    int R[TR_MAX_JOBS], C[TR_MAX_JOBS];
+    int tile_start[TR_MAX_JOBS + 1];  // prefix sums of the jobs' 64x64 tile counts
+    int n;
+};
+
+__global__ __launch_bounds__(256) void transpose_batch_kernel(TransposeJobs J) {
+    __shared__ uint16_t tile[64][64 + 2];
+    const int b = blockIdx.x;
+    int j = 0;
+    while (j + 1 < J.n && b >= J.tile_start[j + 1]) ++j;
+    const int R = J.R[j], C = J.C[j], tc = (C + 63) / 64;
+    const int t = b - J.tile_start[j], r0 = (t / tc) * 64, c0 = (t % tc) * 64;
+    const int tid = threadIdx.x, v = tid & 7, q = tid >> 3;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int rr = q + 32 * h, r = r0 + rr, c = c0 + 8 * v;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (r < R && c < C) w = *(const u32x4*)(J.src[j] + (int64_t)r * C + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            tile[rr][8 * v + 2 * e] = (uint16_t)(w[e] & 0xffffu);
+            tile[rr][8 * v + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int cc = q + 32 * h, c = c0 + cc, r = r0 + 8 * v;
+        if (c >= C || r >= R) continue;
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w[e] = (uint32_t)tile[8 * v + 2 * e][cc] | ((uint32_t)tile[8 * v + 2 * e + 1][cc] << 16);
+        *(u32x4*)(J.dst[j] + (int64_t)c * R + r) = w;
+    }
+}
+
 __global__ void fill_f32_kernel(float* __restrict__ dst, float val, int64_t n) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         dst[i] = val;
@@ -186,6 +232,43 @@ hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int R, int 
     dim3 grid((unsigned)cdiv(Cc, 64), (unsigned)cdiv(R, 64));
     PROF_LAUNCH(KC_TRANSPOSE, 4.0 * R * Cc, s, hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, src, dst, R, Cc));
     return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16_batch(const uint16_t* const* src, uint16_t* const* dst, const int* R,
+                                       const int* Cc, int n, hipStream_t s) {
+    for (int j0 = 0; j0 < n; j0 += TR_MAX_JOBS) {
+        const int m = std::min(TR_MAX_JOBS, n - j0);
+        bool vec = true;
+        for (int j = j0; j < j0 + m; ++j) vec = vec && R[j] % 8 == 0 && Cc[j] % 8 == 0;
+        if (!vec) {  // odd shapes: one scalar transpose each
+            for (int j = j0; j < j0 + m; ++j) {
+                hipError_t e = launch_transpose_bf16(src[j], dst[j], R[j], Cc[j], s);
+                if (e != hipSuccess) return e;
+            }
+            continue;
+        }
+        TransposeJobs J{};
+        J.n = m;
+        int64_t tiles = 0;
+        double bytes = 0;
+        for (int i = 0; i < m; ++i) {
+            J.src[i] = src[j0 + i];
+            J.dst[i] = dst[j0 + i];
+            J.R[i] = R[j0 + i];
+            J.C[i] = Cc[j0 + i];
+            J.tile_start[i] = (int)tiles;
+            tiles += cdiv(R[j0 + i], 64) * cdiv(Cc[j0 + i], 64);
+            bytes += 4.0 * R[j0 + i] * Cc[j0 + i];
+        }
+        J.tile_start[m] = (int)tiles;
+        if (tiles == 0) continue;
+        if (tiles > INT32_MAX) return hipErrorInvalidValue;
+        PROF_LAUNCH(KC_TRANSPOSE, bytes, s,
+                    hipLaunchKernelGGL(transpose_batch_kernel, dim3((unsigned)tiles), dim3(256), 0, s, J));
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_fill_f32(float* dst, float val, int64_t n, hipStream_t s) {

@@ -96,6 +96,9 @@ hipError_t launch_clip_adamw(float* p, float* g, float* m, float* v, uint16_t* s
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 // dst[c][r] = src[r][c] for a bf16 [R, Cc] matrix.
 hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int R, int Cc, hipStream_t s);
+// n transposes dst[j] = src[j]^T (R[j] x Cc[j] row-major in, Cc[j] x R[j] out) in as few launches as possible
+hipError_t launch_transpose_bf16_batch(const uint16_t* const* src, uint16_t* const* dst, const int* R,
+                                       const int* Cc, int n, hipStream_t s);
 hipError_t launch_fill_f32(float* dst, float val, int64_t n, hipStream_t s);
 // dst[e] = float32(std * N(0,1) draw (seed, tensor, e)) for e in [0, n); rows >= zero_from_row (of
 // width cols) are set to 0.
