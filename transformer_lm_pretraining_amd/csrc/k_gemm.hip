@@ -484,10 +484,27 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_w8_kernel(GemmParams p) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(bfr[b][j], af[b][i], acc[i][j]);
     };
+    // second epilogue input for the whole tile: thread tid covers 16-byte chunk
+    // (tid & 31) of rows 16*it + tid/32.  The first PIN_EARLY chunks are read at the
+    // top of the last stage, so their latency hides behind its products.
+    constexpr int EIT = BIG * BIG / 8 / 512;
+    constexpr bool HAS_IN = EPI == EPI_DGELU || EPI == EPI_BF16R;
+    constexpr int PIN_EARLY = HAS_IN ? 8 : 0;
+    u32x4 pin[HAS_IN ? EIT : 1];
+    auto load_pin = [&](int it) {
+        const int grow = m0 + it * 16 + (tid >> 5), gcol = n0 + (tid & 31) * 8;
+        pin[it] = (grow < p.M && gcol < p.N) ? *(const u32x4*)(p.res + (int64_t)grow * p.ldr + gcol) : u32x4{0u, 0u, 0u, 0u};
+    };
     read(smem, 0, 0);
     int s = 0;
     do {
         const uint16_t* st = smem + (s % NS) * St::ELEMS;
+        if constexpr (HAS_IN) {
+            if (s == nk - 1) {
+#pragma unroll
+                for (int it = 0; it < PIN_EARLY; ++it) load_pin(it);
+            }
+        }
 #pragma unroll
         for (int kk = 0; kk < St::KS; ++kk) {
             const int b = kk & 1;
@@ -512,17 +529,10 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_w8_kernel(GemmParams p) {
     __syncthreads();
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
-    // second epilogue input for the whole tile, read now so its latency overlaps
-    // the staging: thread tid covers 16-byte chunk (tid & 31) of rows 16*it + tid/32.
-    constexpr int EIT = BIG * BIG / 8 / 512;
-    constexpr bool HAS_IN = EPI == EPI_DGELU || EPI == EPI_BF16R;
-    u32x4 pin[HAS_IN ? EIT : 1];
+    // the rest of the second epilogue input, read now so its latency overlaps the staging
     if constexpr (HAS_IN) {
 #pragma unroll
-        for (int it = 0; it < EIT; ++it) {
-            const int grow = m0 + it * 16 + (tid >> 5), gcol = n0 + (tid & 31) * 8;
-            pin[it] = (grow < p.M && gcol < p.N) ? *(const u32x4*)(p.res + (int64_t)grow * p.ldr + gcol) : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int it = PIN_EARLY; it < EIT; ++it) load_pin(it);
     }
 
     // stage 1: acc -> bf16 tile [256][256] in LDS (16-byte chunks XOR-swizzled by row)
