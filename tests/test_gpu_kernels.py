@@ -206,7 +206,10 @@ def test_gemm_nt_gelu_parity(gpu_lib, M):
     assert np.max(np.abs(host(gprime) - ops.gelu_grad(ref))) <= 2e-2
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 128, 128), (19456, 768, 768), (2048, 50304, 768), (4096, 768, 3072)])
+# (2048, 712, 768): 9 tiles split over tokens; (512, 3000, 5120): 240 tiles in one pass.  In both the last
+# output-row tile is ragged (200 and 184 of 256 rows), so the bias sums of its waves are partly out of range.
+@pytest.mark.parametrize("M,N,K", [(256, 128, 128), (19456, 768, 768), (2048, 50304, 768), (4096, 768, 3072),
+                                   (2048, 712, 768), (512, 3000, 5120)])
 def test_gemm_tn_acc_parity(gpu_lib, M, N, K):
     import torch
     from transformer_lm_pretraining_amd import lib
