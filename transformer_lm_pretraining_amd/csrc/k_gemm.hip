@@ -29,6 +29,8 @@ namespace {
 constexpr int BK = 64;
 constexpr int LDK = BK + 8;
 constexpr int GROUP_M = 8;
+// weight-gradient tiles: a group of 4 output-row tiles per X column block (measured against 2, 8, 16)
+constexpr int TN_GROUP_M = 4;
 constexpr int NUM_XCD = 8;
 constexpr int NUM_CU = 256;
 
@@ -669,9 +671,9 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(TnGroup G) {
     while (jb + 1 < G.njobs && pid >= G.tile_start[jb + 1]) ++jb;
     pid -= G.tile_start[jb];
     const TnJob p = G.job[jb];
-    const int in_group = GROUP_M * p.tiles_n;
-    const int first_m = (pid / in_group) * GROUP_M;
-    const int gsize = min(p.tiles_m - first_m, GROUP_M);
+    const int in_group = TN_GROUP_M * p.tiles_n;
+    const int first_m = (pid / in_group) * TN_GROUP_M;
+    const int gsize = min(p.tiles_m - first_m, TN_GROUP_M);
     const int tm = first_m + (pid % in_group) % gsize;
     const int tn = (pid % in_group) / gsize;
     const int m0 = tm * BIG, n0 = tn * BIG;  // dY feature (output row) and X feature (output column) origins
