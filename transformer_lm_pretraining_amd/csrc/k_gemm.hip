@@ -58,6 +58,14 @@ struct GemmParams {
     float* dbias;      // TN: bias gradient (column sums of A's source), may be null
 };
 
+// Workgroup ids go round-robin over the XCDs.  Renumbered so that each XCD holds
+// one contiguous run of tiles (XCD x takes total/8 ids, one more when x < total % 8),
+// tiles that share operand slices meet in that XCD's L2 at any tile count.
+__device__ __forceinline__ int xcd_contiguous(int lin, int total) {
+    const int q = total / NUM_XCD, r = total % NUM_XCD, x = lin % NUM_XCD;
+    return x * q + min(x, r) + lin / NUM_XCD;
+}
+
 // Output tile of work-group `lin` among tiles_m x tiles_n.  Work-groups reach
 // the 8 XCDs round-robin by linear index.  With band > 0 each XCD is given one
 // contiguous share of the tile sequence (the first ntiles % 8 XCDs one tile
@@ -67,20 +75,11 @@ struct GemmParams {
 // band = 0 the sequence is dealt round-robin (split into 8 contiguous shares
 // when ntiles is a multiple of 8) over bands of GROUP_M row tiles; for outputs
 // a few tiles wide that keeps every column tile of a row tile on one XCD.
-// Workgroup ids go round-robin over the XCDs.  Renumbered so that each XCD holds
-// one contiguous run of tiles (XCD x takes total/8 ids, one more when x < total % 8),
-// tiles that share operand slices meet in that XCD's L2 at any tile count.
-__device__ __forceinline__ int xcd_contiguous(int lin, int total) {
-    const int q = total / NUM_XCD, r = total % NUM_XCD, x = lin % NUM_XCD;
-    return x * q + min(x, r) + lin / NUM_XCD;
-}
-
 __device__ __forceinline__ void nt_tile(int lin, int tiles_m, int tiles_n, int band, int& tm, int& tn) {
     const int ntiles = tiles_m * tiles_n;
     int pid;
     if (band > 0) {
-        const int q = ntiles / NUM_XCD, r = ntiles % NUM_XCD, x = lin % NUM_XCD;
-        pid = x * q + min(x, r) + lin / NUM_XCD;
+        pid = xcd_contiguous(lin, ntiles);
     } else {
         band = GROUP_M;
         pid = (ntiles % NUM_XCD) == 0 ? (lin % NUM_XCD) * (ntiles / NUM_XCD) + lin / NUM_XCD : lin;
