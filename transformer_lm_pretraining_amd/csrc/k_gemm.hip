@@ -336,8 +336,6 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* src, uint16_t* dst_wav
 #ifndef TN_TD
 #define TN_TD 32
 #endif
-constexpr int PBK = 32;                  // reduction depth of one stage
-constexpr int PSTAGE = 2 * BIG * PBK;    // A and B tiles of one stage, bf16 elements (32 KB)
 
 // Read one accumulator element out of its AGPR where it is needed, so the
 // epilogue never asks for all 256 accumulators in VGPRs at once (which makes
@@ -851,19 +849,6 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(TnGroup G) {
                 }
             }
         }
-    }
-}
-
-// dW += sum over splits of the partials (float4 vectors).
-__global__ void splitk_reduce_kernel(const float4* __restrict__ part, float4* __restrict__ dw, int64_t n4,
-                                     int splits, int64_t stride4) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
-        float4 a = dw[i];
-        for (int s = 0; s < splits; ++s) {
-            float4 b = part[s * stride4 + i];
-            a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-        }
-        dw[i] = a;
     }
 }
 
