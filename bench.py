@@ -71,8 +71,9 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(L, H, C, V, Vp, Tmax, T_sample=256, n_adam=1 << 22, tokens_per_step=175104):
-    """The oracle (NumPy fp32) on the host cores: one sequence of T_sample tokens
+def cpu_baseline(L, H, C, V, Vp, Tmax, T_sample, n_adam=1 << 24, tokens_per_step=175104):
+    """The oracle (NumPy fp32) on the host cores: one whole sequence of T_sample tokens
+    (the workload's sequence length, so attention's quadratic term is at full size)
     forward+backward through the full model, plus clip+AdamW on n_adam parameters,
     scaled to the whole parameter count and amortised over the step's tokens."""
     import numpy as np
@@ -134,8 +135,8 @@ def main():
 
     import numpy as np
     import torch
-    import oracle
     from transformer_lm_pretraining_amd import lib, synth
+    from transformer_lm_pretraining_amd.train import lr_at
 
     L, H, C, V, Vp, Tmax, B, T, n_micro = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
@@ -157,7 +158,7 @@ def main():
             tgt = data[base + 1:base + 1 + BT].view(B, T)
             model.forward(tok, tgt, dloss=dloss, loss_out=losses[k:k + 1])
             model.backward()
-        model.clip_adamw(oracle.lr_at(t_adam), t_adam)
+        model.clip_adamw(lr_at(t_adam), t_adam)
 
     say(f"bench: {args.workload} B={B} T={T} x{n_micro} micro-steps; warmup {args.warmup}, timed {args.steps}")
     for i in range(args.warmup):
@@ -250,7 +251,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         say("timing the CPU oracle on a bounded sample ...")
-        out["cpu_baseline"] = cpu_baseline(L, H, C, V, Vp, Tmax, tokens_per_step=tokens_per_step)
+        out["cpu_baseline"] = cpu_baseline(L, H, C, V, Vp, Tmax, T_sample=T, tokens_per_step=tokens_per_step)
     print(json.dumps(out), flush=True)
 
 

@@ -246,8 +246,8 @@ def test_zero_embedding_loss_is_ln_V_gpu(gpu_lib):
 @pytest.mark.parametrize("L,B", [(2, 2), (3, 1)])
 def test_gpt2_shapes_two_layers_parity(gpu_lib, L, B):
     """The 124M layer shapes (C=768, 12 heads of 64, T=1024, Vp=50,304) at 2 layers, B=2,
-    and at 3 layers, B=1 (the weight gradients of two blocks go out in one launch; with
-    an odd layer count the first block's go alone)."""
+    and at 3 layers, B=1 (all blocks' weight gradients go out in one grouped launch after
+    the last block, with a different split of its tail at each size)."""
     import torch
     cfg = Config(L=L, H=12, C=768, V=50257, Vp=50304, Tmax=1024)
     T = 1024
@@ -341,3 +341,96 @@ def test_gpt2_124m_full_size_sampled(gpu_lib):
     assert math.isfinite(n) and n > 0
     wte = model.tensor(model.params, "wte").cpu().numpy()
     assert np.all(wte[cfg.V:] == 0)
+
+
+@pytest.mark.timeout(600)
+def test_gpt2_124m_production_shape_all_gradients(gpu_lib):
+    """PDS's four-level check at the benchmarked shape: GPT-2 124M, B = 19, T = 1,024, two
+    accumulated micro-steps, then clip + AdamW.  The GPU runs the full plan of that shape
+    (every GEMM at its real size, the 48-product grouped weight-gradient launch and its
+    token-split tail, the lm_head weight gradient's split rows, the token-table sort over
+    19,456 rows).  Targets are ignored except in sequences 0, 9 and 18 of the first
+    micro-step and sequence 18 of the second: those rows alone carry gradient (attention
+    never mixes sequences), so the fp32 oracle computes just them.  Checked: the residual
+    stream after every block, the kept rows' losses, all 148 accumulated gradients
+    (relative L2 <= 3e-2, cosine >= 0.999, padding rows exactly 0), and AdamW at t = 5 from
+    non-zero moments on the GPU's own gradients (p, m, v within 1e-6 relative; bf16 shadow
+    = RNE(p) bitwise)."""
+    import torch
+    from transformer_lm_pretraining_amd import lib
+    cfg = CONFIGS["gpt2_124m"]
+    B, T, n_micro = 19, 1024, 2
+    keep = [[0, 9, 18], [18]]
+    say("gpt2 124M production shape: init")
+    P = init_params(cfg, 1337)
+    flat = oracle.flatten(cfg, P)
+    batches = synth.micro_batches(n_micro, B, T, cfg.V, seed=41)
+    model = make_model(cfg, B, T, init=flat)
+    dloss = 1.0 / (B * T * n_micro)
+    gpu_rows, gpu_resid = [], None
+    for k, (tok, tgt) in enumerate(batches):
+        t = np.full_like(tgt, lib.IGNORE_TARGET)
+        t[keep[k]] = tgt[keep[k]]
+        model.forward(to_dev_i32(tok), to_dev_i32(t), dloss=dloss)
+        gpu_rows.append(host(model.row_losses()).reshape(B, T))
+        if k == 0:
+            gpu_resid = [host(model.residual(l)).reshape(B, T, cfg.C)[keep[0]] for l in range(cfg.L + 1)]
+        model.backward()
+    grads = model.grads.cpu().numpy().copy()
+    assert model.sync_status() == lib.GPT2_OK
+    say("gpu done; oracle micro-steps")
+    G_ref = None
+    for k, (tok, tgt) in enumerate(batches):
+        s = keep[k]
+        _, ref_rows, cache = forward(cfg, P, tok[s], tgt[s], dtype=np.float32)
+        G = backward(cfg, P, cache, dloss, dtype=np.float32)
+        rows = gpu_rows[k]
+        ign = np.ones(B, bool)
+        ign[s] = False
+        assert np.all(rows[ign] == 0), "ignored rows carry no loss"
+        assert np.max(np.abs(rows[s] - ref_rows)) <= 0.15
+        assert abs(rows[s].mean() - ref_rows.mean()) <= 2e-2, (rows[s].mean(), ref_rows.mean())
+        if k == 0:
+            for l in range(cfg.L + 1):
+                r = rel_l2(gpu_resid[l], cache["resid"][l])
+                assert r <= 1e-2, (l, r)
+        G_ref = G if G_ref is None else {n: G_ref[n] + G[n] for n in G}
+        say("oracle micro-step", k, "done")
+    Gg = {}
+    for name, off, rows_, cols, _, _ in model.table:
+        a = grads[off:off + rows_ * cols]
+        Gg[name] = a.reshape(rows_, cols) if rows_ > 1 else a
+    assert len(Gg) == 148
+    check_grads(Gg, G_ref, cfg, T)
+    # AdamW at t = 5 from non-zero moments, on the GPU's own accumulated gradients.  Errors
+    # are measured against the magnitudes entering each stored value (the moments' two
+    # terms may cancel; fp32 rounding is relative to the terms, not to their sum).
+    rs = np.random.default_rng(5)
+    n = grads.size
+    m0 = (rs.standard_normal(n) * 1e-4).astype(np.float32)
+    v0 = (m0.astype(np.float64) ** 2 * (0.5 + rs.random(n)) + 1e-14).astype(np.float32)
+    p0 = model.params.cpu().numpy().copy()
+    model.m.copy_(torch.from_numpy(m0).cuda())
+    model.v.copy_(torch.from_numpy(v0).cuda())
+    lr, t_adam = 3e-4, 5
+    norm = model.clip_adamw(lr, t_adam)
+    torch.cuda.synchronize()
+    mask = np.zeros(n, bool)
+    mask[:model.sz.n_decay] = True
+    pr, mr, vr, nr = oracle.clip_adamw(p0, grads, m0, v0, mask, t_adam, lr)
+    say("norm gpu", float(norm.item()), "oracle", nr)
+    assert abs(float(norm.item()) - nr) <= 1e-6 * nr
+    gc = grads.astype(np.float64) * min(1.0, 1.0 / nr)
+    mag_m = 0.9 * np.abs(m0.astype(np.float64)) + 0.1 * np.abs(gc)
+    mag_v = 0.95 * v0.astype(np.float64) + 0.05 * gc * gc
+    got_p = model.params.cpu().numpy().astype(np.float64)
+    got_m = model.m.cpu().numpy().astype(np.float64)
+    got_v = model.v.cpu().numpy().astype(np.float64)
+    p064, pr64 = p0.astype(np.float64), pr.astype(np.float64)
+    assert np.all(np.abs(got_m - mr) <= 1e-6 * mag_m + 1e-30)
+    assert np.all(np.abs(got_v - vr) <= 1e-6 * mag_v + 1e-30)
+    assert np.all(np.abs(got_p - pr64) <= 1e-6 * (np.abs(p064) + np.abs(pr64 - p064)) + 1e-30)
+    sh = model.shadow.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(sh, bf16_rne_bits(model.params.cpu().numpy()[:model.sz.n_decay]))
+    assert np.all(model.grads.cpu().numpy() == 0)
+    assert np.all(model.tensor(model.params, "wte").cpu().numpy()[cfg.V:] == 0)

@@ -121,6 +121,65 @@ def test_adamw_constant_gradient_from_zero_state():
     np.testing.assert_allclose(v1, 0.05 * g.astype(np.float64) ** 2, rtol=1e-12)
 
 
+def test_adamw_constant_gradient_carried_over_six_steps():
+    """Constant g from zero moments: m_t = (1 - 0.9^t) g and v_t = (1 - 0.95^t) g^2
+    (geometric sums), so the bias-corrected mhat = g and vhat = g^2 at every t and each
+    update is lr_t (g / (|g| + eps) + wd p).  The moments carried between steps and the
+    exponent t of the bias correction both enter; a swapped beta or an off-by-one in t
+    moves mhat away from g."""
+    rs = np.random.default_rng(10)
+    n = 512
+    p = rs.standard_normal(n) * 0.02
+    g = rs.standard_normal(n) * 1e-3  # ||g|| < 1: no clipping
+    mask = np.arange(n) < 300
+    wd = np.where(mask, 0.1, 0.0)
+    m = np.zeros(n)
+    v = np.zeros(n)
+    want_p = p.copy()
+    for t in range(1, 7):
+        lr = 1e-4 * t  # a different rate at every step
+        p, m, v, _ = oracle.clip_adamw(p, g, m, v, mask, t, lr, dtype=np.float64)
+        np.testing.assert_allclose(m, (1 - 0.9 ** t) * g, rtol=1e-13)
+        np.testing.assert_allclose(v, (1 - 0.95 ** t) * g * g, rtol=1e-13)
+        want_p = want_p - lr * (g / (np.abs(g) + 1e-8) + wd * want_p)
+        np.testing.assert_allclose(p, want_p, rtol=1e-12, atol=1e-16)
+
+
+def test_adamw_two_steps_hand_expanded():
+    """Two different gradients, written out by hand: after step 1, m1 = 0.1 g1 and
+    v1 = 0.05 g1^2; after step 2, m2 = 0.9 * 0.1 g1 + 0.1 g2 and
+    v2 = 0.95 * 0.05 g1^2 + 0.05 g2^2, corrected by 1 - 0.9^2 = 0.19 and
+    1 - 0.95^2 = 0.0975.  The second gradient has norm 2.5, so it is clipped to
+    unit norm before it enters the moments."""
+    p0 = np.array([0.5, -0.25, 0.125, 2.0])
+    g1 = np.array([0.3, -0.2, 0.1, 0.0])       # norm 0.374 < 1
+    g2 = np.array([1.5, 0.0, -2.0, 0.0])       # norm 2.5 -> scaled by 0.4
+    mask = np.array([True, True, False, False])
+    lr1, lr2 = 1e-3, 2e-3
+    p1, m1, v1, n1 = oracle.clip_adamw(p0, g1, np.zeros(4), np.zeros(4), mask, 1, lr1, dtype=np.float64)
+    assert n1 == pytest.approx(math.sqrt(0.09 + 0.04 + 0.01), rel=1e-15)
+    np.testing.assert_allclose(m1, [0.03, -0.02, 0.01, 0.0], rtol=1e-14, atol=0)
+    np.testing.assert_allclose(v1, [0.0045, 0.002, 0.0005, 0.0], rtol=1e-14, atol=0)
+    # mhat1 = g1, vhat1 = g1^2: the update is lr1 * (sign(g1) + wd p0) up to eps
+    want1 = np.array([0.5 - lr1 * (0.3 / (0.3 + 1e-8) + 0.1 * 0.5),
+                      -0.25 - lr1 * (-0.2 / (0.2 + 1e-8) + 0.1 * -0.25),
+                      0.125 - lr1 * (0.1 / (0.1 + 1e-8)),
+                      2.0])
+    np.testing.assert_allclose(p1, want1, rtol=1e-15)
+    p2, m2, v2, n2 = oracle.clip_adamw(p1, g2, m1, v1, mask, 2, lr2, dtype=np.float64)
+    assert n2 == pytest.approx(2.5, rel=1e-15)
+    # g2 / 2.5 = [0.6, 0, -0.8, 0]
+    want_m2 = np.array([0.9 * 0.03 + 0.1 * 0.6, 0.9 * -0.02, 0.9 * 0.01 + 0.1 * -0.8, 0.0])
+    want_v2 = np.array([0.95 * 0.0045 + 0.05 * 0.36, 0.95 * 0.002, 0.95 * 0.0005 + 0.05 * 0.64, 0.0])
+    np.testing.assert_allclose(m2, want_m2, rtol=1e-14, atol=0)
+    np.testing.assert_allclose(v2, want_v2, rtol=1e-14, atol=0)
+    mhat = want_m2 / 0.19
+    vhat = want_v2 / 0.0975
+    step = mhat / (np.sqrt(vhat) + 1e-8) + np.array([0.1, 0.1, 0.0, 0.0]) * want1
+    np.testing.assert_allclose(p2, want1 - lr2 * step, rtol=1e-14)
+    assert p2[3] == 2.0  # no gradient, no decay: untouched
+
+
 def test_adamw_zero_gradient_is_pure_decay():
     p = np.linspace(-1, 1, 64).astype(np.float64)
     mask = np.arange(64) < 32

@@ -323,19 +323,11 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* src, uint16_t* dst_wav
 
 // ---------------------------------------------------------------------------
 // Shared pieces of the pipelined 256x256 kernels.  Stage depth and count are
-// build-time constants (NT: 2 stages of 64 reduction columns; TN: 4 of 32 tokens).
-#ifndef NT_STAGES
-#define NT_STAGES 2
-#endif
-#ifndef NT_KD
-#define NT_KD 64
-#endif
-#ifndef TN_STAGES
-#define TN_STAGES 4
-#endif
-#ifndef TN_TD
-#define TN_TD 32
-#endif
+// fixed: NT runs 2 stages of 64 reduction columns, TN 4 stages of 32 tokens.
+constexpr int NT_STAGES = 2;
+constexpr int NT_KD = 64;
+constexpr int TN_STAGES = 4;
+constexpr int TN_TD = 32;
 
 // Read one accumulator element out of its AGPR where it is needed, so the
 // epilogue never asks for all 256 accumulators in VGPRs at once (which makes
