@@ -132,6 +132,21 @@ int gpt2k_clip_adamw(float* p, float* g, float* m, float* v, uint16_t* shadow, i
                      hipStream_t stream);
 
 /*
+ * gpt2k_clip_adamw without a scratch argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight training loops,
+ * harnesses that forbid hipMalloc).  Same arguments, semantics and results as
+ * gpt2k_clip_adamw; it allocates nothing.  Its scratch (the clip scale and
+ * the fp64 partial sums of the squared gradient) is a fixed 16 KiB device
+ * array inside the library, one copy per GPU, kept until the process ends;
+ * sizes whose scratch would not fit return GPT2_E_SHAPE (at present every n
+ * fits: the partial-sum count does not grow with n).  All calls on one GPU
+ * share that GPU's copy: calls that overlap on one GPU race.  Errors:
+ * GPT2_E_INVALID (as gpt2k_clip_adamw), GPT2_E_SHAPE, GPT2_E_HIP.
+ */
+int gpt2k_clip_adamw_noalloc(float* p, float* g, float* m, float* v, uint16_t* shadow, int64_t n, int64_t n_decay,
+                             const gpt2_adamw_args* args, float* norm_dev, hipStream_t stream);
+
+/*
  * Token + position embedding: x[r] = wte[tok[r]] + wpe[r % T] (bf16 tables,
  * bf16 out [B*T, C]).  Ids outside [0, V) set *flag and are clamped.
  */

@@ -89,6 +89,8 @@ _SIGS = {
     "gpt2k_attention_bwd": (c_int32, [c_void_p] * 6 + [c_int32] * 4 + [c_void_p]),
     "gpt2k_clip_adamw": (c_int32, [c_void_p] * 5 + [c_int64, c_int64, POINTER(AdamwArgs), c_void_p, c_void_p,
                                                     c_int64, c_void_p]),
+    "gpt2k_clip_adamw_noalloc": (c_int32, [c_void_p] * 5 + [c_int64, c_int64, POINTER(AdamwArgs), c_void_p,
+                                            c_void_p]),
     "gpt2k_embedding_fwd": (c_int32, [c_void_p] * 4 + [c_int32] * 4 + [c_void_p, c_void_p]),
     "gpt2k_embedding_bwd": (c_int32, [c_void_p] * 4 + [c_int32] * 4 + [c_void_p, c_int64, c_void_p]),
     "gpt2k_scratch_bytes": (c_int32, [c_int32, c_int64, c_int64, c_int64, POINTER(c_int64)]),
@@ -404,6 +406,19 @@ def clip_adamw(p, g, m, v, shadow, n_decay, lr, t, beta1=0.9, beta2=0.95, eps=1e
     norm = torch.zeros(1, dtype=torch.float32, device=p.device)
     check(load().gpt2k_clip_adamw(_ptr(p), _ptr(g), _ptr(m), _ptr(v), _ptr(shadow), n, n_decay, ctypes.byref(a),
                                   _ptr(norm), _ptr(s), s.numel(), _stream()), "gpt2k_clip_adamw")
+    return norm
+
+
+def clip_adamw_noalloc(p, g, m, v, shadow, n_decay, lr, t, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
+                       max_norm=1.0, norm=None):
+    """gpt2k_clip_adamw_noalloc: the library's own static scratch; norm (fp32 device
+    scalar) must be given by a caller that allocates nothing here."""
+    import torch
+    a = AdamwArgs(lr, beta1, beta2, eps, weight_decay, max_norm, t)
+    if norm is None:
+        norm = torch.zeros(1, dtype=torch.float32, device=p.device)
+    check(load().gpt2k_clip_adamw_noalloc(_ptr(p), _ptr(g), _ptr(m), _ptr(v), _ptr(shadow), p.numel(), n_decay,
+                                          ctypes.byref(a), _ptr(norm), _stream()), "gpt2k_clip_adamw_noalloc")
     return norm
 
 
