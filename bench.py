@@ -71,8 +71,8 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(L, H, C, V, Vp, Tmax, T_sample, n_adam=1 << 24, tokens_per_step=175104):
-    """The oracle (NumPy fp32) on the host cores: one whole sequence of T_sample tokens
+def cpu_baseline(L, H, C, V, Vp, Tmax, T_sample, B_sample=3, n_adam=1 << 24, tokens_per_step=175104):
+    """The oracle (NumPy fp32) on the host cores: B_sample whole sequences of T_sample tokens
     (the workload's sequence length, so attention's quadratic term is at full size)
     forward+backward through the full model, plus clip+AdamW on n_adam parameters,
     scaled to the whole parameter count and amortised over the step's tokens."""
@@ -84,7 +84,7 @@ def cpu_baseline(L, H, C, V, Vp, Tmax, T_sample, n_adam=1 << 24, tokens_per_step
     P = {}
     for i, (name, shape, dec) in enumerate(tensor_specs(cfg)):
         P[name] = synth.normal(shape, std=0.02, seed=1000 + i) if dec else np.ones(shape, np.float32)
-    tok, tgt = synth.micro_batches(1, 1, T_sample, V, seed=5)[0]
+    tok, tgt = synth.micro_batches(1, B_sample, T_sample, V, seed=5)[0]
     t0 = time.perf_counter()
     oracle.loss_and_grads(cfg, P, tok, tgt, dtype=np.float32)
     t_fb = time.perf_counter() - t0
@@ -95,10 +95,10 @@ def cpu_baseline(L, H, C, V, Vp, Tmax, T_sample, n_adam=1 << 24, tokens_per_step
     oracle.clip_adamw(p, g, z, z, np.ones(n_adam, bool), 350, oracle.lr_at(350))
     t_adam = time.perf_counter() - t0
     n_params = oracle.n_params(cfg)
-    t_tok = t_fb / T_sample + t_adam * (n_params / n_adam) / tokens_per_step
+    t_tok = t_fb / (B_sample * T_sample) + t_adam * (n_params / n_adam) / tokens_per_step
     cores = len(os.sched_getaffinity(0))
     return {"value": round(1.0 / t_tok, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": (f"full model, 1 sequence x {T_sample} tokens forward+backward in fp32 ({t_fb:.1f} s) "
+            "sample": (f"full model, {B_sample} sequences x {T_sample} tokens forward+backward in fp32 ({t_fb:.1f} s) "
                        f"+ clip/AdamW on {n_adam} params ({t_adam:.2f} s) scaled to {n_params} params "
                        f"and amortised over {tokens_per_step} tokens/step")}
 

@@ -352,7 +352,8 @@ def test_gpt2_124m_production_shape_all_gradients(gpu_lib):
     19,456 rows).  Targets are ignored except in sequences 0, 9 and 18 of the first
     micro-step and sequence 18 of the second: those rows alone carry gradient (attention
     never mixes sequences), so the fp32 oracle computes just them.  Checked: the residual
-    stream after every block, the kept rows' losses, all 148 accumulated gradients
+    stream after every block (within the bf16 rounding it accumulates with depth), the
+    kept rows' losses, all 148 accumulated gradients
     (relative L2 <= 3e-2, cosine >= 0.999, padding rows exactly 0), and AdamW at t = 5 from
     non-zero moments on the GPU's own gradients (p, m, v within 1e-6 relative; bf16 shadow
     = RNE(p) bitwise)."""
@@ -391,9 +392,14 @@ def test_gpt2_124m_production_shape_all_gradients(gpu_lib):
         assert np.max(np.abs(rows[s] - ref_rows)) <= 0.15
         assert abs(rows[s].mean() - ref_rows.mean()) <= 2e-2, (rows[s].mean(), ref_rows.mean())
         if k == 0:
-            for l in range(cfg.L + 1):
-                r = rel_l2(gpu_resid[l], cache["resid"][l])
-                assert r <= 1e-2, (l, r)
+            # bf16 residual stream: the embedding and each block's four roundings (two
+            # sub-layer outputs, two residual adds) of at most 2^-8 relative, rms 2^-8/sqrt(3)
+            # each, add up in quadrature over l blocks; the bound is that with a 1.5x margin
+            # and never below the 1e-2 of the shallow models
+            rs_ = [rel_l2(gpu_resid[l], cache["resid"][l]) for l in range(cfg.L + 1)]
+            say("residual stream rel L2 by depth:", np.round(rs_, 5))
+            for l, r in enumerate(rs_):
+                assert r <= max(1e-2, 1.5 * 2.0 ** -8 / math.sqrt(3) * math.sqrt(4 * l + 1)), (l, r)
         G_ref = G if G_ref is None else {n: G_ref[n] + G[n] for n in G}
         say("oracle micro-step", k, "done")
     Gg = {}
@@ -409,6 +415,10 @@ def test_gpt2_124m_production_shape_all_gradients(gpu_lib):
     n = grads.size
     m0 = (rs.standard_normal(n) * 1e-4).astype(np.float32)
     v0 = (m0.astype(np.float64) ** 2 * (0.5 + rs.random(n)) + 1e-14).astype(np.float32)
+    # the padding rows of wte never get a gradient, so their moments stay 0 in a run
+    pad = slice(cfg.V * cfg.C, cfg.Vp * cfg.C)  # wte is the first tensor of the flat layout
+    m0[pad] = 0.0
+    v0[pad] = 0.0
     p0 = model.params.cpu().numpy().copy()
     model.m.copy_(torch.from_numpy(m0).cuda())
     model.v.copy_(torch.from_numpy(v0).cuda())
@@ -429,7 +439,11 @@ def test_gpt2_124m_production_shape_all_gradients(gpu_lib):
     p064, pr64 = p0.astype(np.float64), pr.astype(np.float64)
     assert np.all(np.abs(got_m - mr) <= 1e-6 * mag_m + 1e-30)
     assert np.all(np.abs(got_v - vr) <= 1e-6 * mag_v + 1e-30)
-    assert np.all(np.abs(got_p - pr64) <= 1e-6 * (np.abs(p064) + np.abs(pr64 - p064)) + 1e-30)
+    # p: relative to |p| plus the size of the update's terms (where the moment's terms
+    # cancel, mhat is small but its fp32 error is relative to those terms)
+    upd = lr * ((mag_m / (1 - 0.9 ** t_adam)) / (np.sqrt(vr.astype(np.float64) / (1 - 0.95 ** t_adam)) + 1e-8)
+                + 0.1 * np.abs(p064))
+    assert np.all(np.abs(got_p - pr64) <= 1e-6 * np.maximum(np.abs(pr64), np.abs(p064) + upd) + 1e-30)
     sh = model.shadow.view(torch.int16).cpu().numpy().view(np.uint16)
     np.testing.assert_array_equal(sh, bf16_rne_bits(model.params.cpu().numpy()[:model.sz.n_decay]))
     assert np.all(model.grads.cpu().numpy() == 0)
