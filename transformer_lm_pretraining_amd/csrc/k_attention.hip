@@ -64,18 +64,35 @@ __device__ __forceinline__ const bf16x8& frag_rows(const uint16_t* tile, int ld,
     return *(const bf16x8*)(tile + (row0 + (lane & 31)) * ld + kk * 16 + (lane >> 5) * 8);
 }
 
-// Register staging of a 64 x D block of one qkv/dout third (rows row0.., columns col..).
+// Register staging of a 64 x D block of one qkv/dout third through buffer loads.
+// The resource holds the operand's base for this sequence and head; each
+// thread's byte offsets within a block are fixed and a block's first row enters
+// as the scalar offset, so a block costs no per-thread address arithmetic.
+constexpr int BUF_DWORD3 = 0x00020000;  // buffer resource word 3 for gfx9-family raw loads
+
 template <int D>
 struct Stage {
     static constexpr int NV = KVB * D / 8 / 256;
     static_assert(NV >= 1, "at least one vector per thread");
     u32x4 v[NV];
-    __device__ __forceinline__ void load(const uint16_t* g, int64_t ld, int row0, int tid) {
+    int voff[NV];
+    int row_bytes;
+    __amdgpu_buffer_rsrc_t rs;
+    // base: element (row 0, column 0) of the operand; ld: row stride in elements;
+    // rows: rows addressable from base (every block lies inside them)
+    __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int rows, int tid) {
+        row_bytes = (int)ld * 2;
+        rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (rows - 1) * row_bytes + D * 2, BUF_DWORD3);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int vid = tid + 256 * i, r = vid / (D / 8), c = vid % (D / 8);
-            v[i] = *(const u32x4*)(g + (int64_t)(row0 + r) * ld + c * 8);
+            voff[i] = r * row_bytes + c * 16;
         }
+    }
+    __device__ __forceinline__ void load(int row0) {
+        const int so = row0 * row_bytes;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i], so, 0);
     }
     __device__ __forceinline__ void store(uint16_t* s, int tid) const {
 #pragma unroll
@@ -135,8 +152,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     const int nkv = q_last / KVB + 1;
     const int q_last_w = min(qw + 31, T - 1);
     Stage<D> stk, stv;
-    stk.load(Kg, ld, 0, tid);
-    stv.load(Vg, ld, 0, tid);
+    stk.init(Kg, ld, T, tid);
+    stv.init(Vg, ld, T, tid);
+    stk.load(0);
+    stv.load(0);
     stk.store(sK[0], tid);
     stv.store(sV[0], tid);
     __syncthreads();
@@ -144,8 +163,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
         const int buf = kb & 1;
         const int s0 = kb * KVB;
         if (kb + 1 < nkv) {
-            stk.load(Kg, ld, s0 + KVB, tid);
-            stv.load(Vg, ld, s0 + KVB, tid);
+            stk.load(s0 + KVB);
+            stv.load(s0 + KVB);
         }
         if (qw < T && s0 <= q_last_w) {
             floatx16 sacc[2];
@@ -290,10 +309,12 @@ __global__ __launch_bounds__(256, 2) void attn_dkdv_kernel(const uint16_t* __res
     const int i_first = k0;  // k0 is a multiple of 128 below T
     const int nqb = (T - i_first) / KVB;
     Stage<D> stq, sto;
+    stq.init(Qg, ld, T, tid);
+    sto.init(dOg, C, T, tid);
     float rl = 0.f, rd = 0.f;
     auto load_block = [&](int i0) {
-        stq.load(Qg, ld, i0, tid);
-        sto.load(dOg, C, i0, tid);
+        stq.load(i0);
+        sto.load(i0);
         if (tid < KVB) {
             rl = lse_bh[i0 + tid] * LOG2E;
             rd = dv_bh[i0 + tid];
@@ -461,8 +482,10 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const uint16_t* __restr
     const int nkv = q_last / KVB + 1;
     const int q_last_w = min(qw + 31, T - 1);
     Stage<D> stk, stv;
-    stk.load(Kg, ld, 0, tid);
-    stv.load(Vg, ld, 0, tid);
+    stk.init(Kg, ld, T, tid);
+    stv.init(Vg, ld, T, tid);
+    stk.load(0);
+    stv.load(0);
     float dvi = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
@@ -480,8 +503,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const uint16_t* __restr
         const int buf = kb & 1;
         const int s0 = kb * KVB;
         if (kb + 1 < nkv) {
-            stk.load(Kg, ld, s0 + KVB, tid);
-            stv.load(Vg, ld, s0 + KVB, tid);
+            stk.load(s0 + KVB);
+            stv.load(s0 + KVB);
         }
         if (qw < T && s0 <= q_last_w) {
 #pragma unroll

@@ -499,11 +499,23 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_w8_kernel(GemmParams p) {
 #pragma unroll
         for (int kk = 0; kk < St::KS; ++kk) {
             const int b = kk & 1;
+            if (kk + 1 < St::KS) {
+                mma(b, 0);
+                read(st, kk + 1, b ^ 1);
+                mma(b, 2);
+                // the next k-step's 6 reads spread over all 8 products
+#pragma unroll
+                for (int q = 0; q < 6; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                continue;
+            }
             mma(b, 0);
             __builtin_amdgcn_sched_barrier(0);
-            if (kk + 1 < St::KS) {
-                read(st, kk + 1, b ^ 1);
-            } else if (s + 1 < nk) {
+            if (s + 1 < nk) {
                 // stage s+1 has landed once only the stages issued after it remain in flight
                 wait_stage_groups<2 * IPO>(min(s + NS - 1, nk - 1) - (s + 1));
                 __syncthreads();
@@ -761,6 +773,17 @@ __global__ __launch_bounds__(512, 1) void gemm_tn_w8_kernel(TnGroup G) {
                 __builtin_amdgcn_sched_barrier(0);
                 if (kk + 1 < KS) {
                     read_frags(st, kk + 1, b ^ 1);
+                    mma(b, 2);
+                    // 12 transposed reads spread over the 4 products
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (decltype(bias_frag)::value >= 0) add_bias(b, bias_frag);
+                    __builtin_amdgcn_sched_barrier(0);
+                    continue;
                 } else if (s + 1 < nk) {
                     // stage s+1 has landed once only the NS-2 groups issued after it remain
                     __builtin_amdgcn_s_waitcnt(vm_imm((NS - 2) * 2 * IPO));
