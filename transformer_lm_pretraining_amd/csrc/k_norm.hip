@@ -102,6 +102,94 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const uint16_t* __restrict_
     }
 }
 
+// Rows of C = 256 NV elements: each half-wave takes one row with 16-byte loads
+// (lane l of the half covers elements (j*32 + l)*8 .. +7), so a wave normalises
+// two rows at a time; sums are taken over the 32 lanes of the half.  Rows walk
+// with a grid stride and the next pair's loads are in flight during the current.
+template <int NV>
+__global__ __launch_bounds__(256) void ln_fwd16_kernel(const uint16_t* __restrict__ x, const float* __restrict__ w,
+                                                       const float* __restrict__ b, uint16_t* __restrict__ y,
+                                                       float* __restrict__ mean_out, float* __restrict__ rstd_out,
+                                                       int64_t rows) {
+    constexpr int C = NV * 256;
+    const int lane = threadIdx.x & 63, hl = lane & 31;
+    float wv[NV][8], bv[NV][8];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const float4* wp = (const float4*)(w + (j * 32 + hl) * 8);
+        const float4* bp = (const float4*)(b + (j * 32 + hl) * 8);
+        const float4 w0 = wp[0], w1 = wp[1], b0 = bp[0], b1 = bp[1];
+        wv[j][0] = w0.x; wv[j][1] = w0.y; wv[j][2] = w0.z; wv[j][3] = w0.w;
+        wv[j][4] = w1.x; wv[j][5] = w1.y; wv[j][6] = w1.z; wv[j][7] = w1.w;
+        bv[j][0] = b0.x; bv[j][1] = b0.y; bv[j][2] = b0.z; bv[j][3] = b0.w;
+        bv[j][4] = b1.x; bv[j][5] = b1.y; bv[j][6] = b1.z; bv[j][7] = b1.w;
+    }
+    auto half_sum = [](float v) {
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+        return v;
+    };
+    auto load = [&](int64_t row, u32x4* xv) {
+        const u32x4* xr = (const u32x4*)(x + row * C);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) xv[j] = xr[j * 32 + hl];
+    };
+    auto compute = [&](int64_t row, const u32x4* xv) {
+        float v[NV][8];
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[j][2 * e] = bflo(xv[j][e]);
+                v[j][2 * e + 1] = bfhi(xv[j][e]);
+            }
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s += v[j][e];
+        const float mean = half_sum(s) * (1.0f / C);
+        float q = 0.f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float d = v[j][e] - mean;
+                q += d * d;
+            }
+        const float var = half_sum(q) * (1.0f / C);
+        const float rstd = 1.0f / sqrtf(var + LN_EPS);
+        u32x4* yr = (u32x4*)(y + row * C);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] = pack_bf2((v[j][2 * e] - mean) * rstd * wv[j][2 * e] + bv[j][2 * e],
+                                (v[j][2 * e + 1] - mean) * rstd * wv[j][2 * e + 1] + bv[j][2 * e + 1]);
+            yr[j * 32 + hl] = o;
+        }
+        if (hl == 0) {
+            mean_out[row] = mean;
+            rstd_out[row] = rstd;
+        }
+    };
+    const int64_t stride = (int64_t)gridDim.x * (2 * ROWS_PER_BLOCK);
+    int64_t row = (int64_t)blockIdx.x * (2 * ROWS_PER_BLOCK) + (threadIdx.x >> 5);
+    u32x4 xa[NV], xb[NV];
+    if (row < rows) load(row, xa);
+    while (row < rows) {
+        const int64_t r1 = row + stride;
+        if (r1 < rows) load(r1, xb);
+        compute(row, xa);
+        if (r1 >= rows) break;
+        const int64_t r2 = r1 + stride;
+        if (r2 < rows) load(r2, xa);
+        compute(r1, xb);
+        row = r2;
+    }
+}
+
 // Each wave walks rows with a grid stride and keeps the next row's loads (x,
 // dy and, when accumulating, the residual gradient) in flight while it
 // computes the current one.
@@ -265,9 +353,17 @@ template <int VEC, int NV>
 hipError_t ln_fwd_t(const uint16_t* x, const float* w, const float* b, uint16_t* y, float* mean, float* rstd,
                     int64_t rows, hipStream_t s) {
     constexpr int C = NV * 64 * VEC;
-    PROF_LAUNCH(KC_LN_FWD, 4.0 * rows * C, s,
-                hipLaunchKernelGGL((ln_fwd_kernel<VEC, NV>), dim3(ln_blocks(rows)), dim3(256), 0, s, x, w, b, y, mean,
-                                   rstd, rows));
+    if constexpr (C % 256 == 0) {
+        // half-wave rows with 16-byte loads: eight rows per block of four waves
+        const int blocks = (int)std::min<int64_t>(768, cdiv(rows, 2 * ROWS_PER_BLOCK));
+        PROF_LAUNCH(KC_LN_FWD, 4.0 * rows * C, s,
+                    hipLaunchKernelGGL((ln_fwd16_kernel<C / 256>), dim3(blocks), dim3(256), 0, s, x, w, b, y, mean,
+                                       rstd, rows));
+    } else {
+        PROF_LAUNCH(KC_LN_FWD, 4.0 * rows * C, s,
+                    hipLaunchKernelGGL((ln_fwd_kernel<VEC, NV>), dim3(ln_blocks(rows)), dim3(256), 0, s, x, w, b, y,
+                                       mean, rstd, rows));
+    }
     return hipGetLastError();
 }
 

@@ -13,15 +13,36 @@ namespace {
 constexpr int NORM_BLOCKS = 1024;
 constexpr int OPT_THREADS = 256;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_nt(const float4* p) {
+    const f32x4 v = __builtin_nontemporal_load((const f32x4*)p);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt(float4* p, float4 v) {
+    __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, (f32x4*)p);
+}
+
 // Per-block sum of squares of g (fp32 per thread, fp64 across the block).
 __global__ __launch_bounds__(OPT_THREADS) void sumsq_kernel(const float4* __restrict__ g, int64_t n4,
                                                             double* __restrict__ partial) {
     __shared__ double red[OPT_THREADS / 64];
-    float s = 0.f;
-    for (int64_t i = blockIdx.x * (int64_t)OPT_THREADS + threadIdx.x; i < n4; i += (int64_t)gridDim.x * OPT_THREADS) {
-        float4 v = g[i];
-        s += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    // four vectors per thread in flight, each in its own accumulator (a fixed order:
+    // the same inputs give the same bits)
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+    const int64_t step = (int64_t)gridDim.x * OPT_THREADS;
+    int64_t i = blockIdx.x * (int64_t)OPT_THREADS + threadIdx.x;
+    for (; i + 3 * step < n4; i += 4 * step) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = g[i + u * step];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s4[u] += v[u].x * v[u].x + v[u].y * v[u].y + v[u].z * v[u].z + v[u].w * v[u].w;
     }
+    for (; i < n4; i += step) {
+        const float4 v = g[i];
+        s4[0] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     double d = wave_sum_d((double)s);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = d;
     __syncthreads();
@@ -65,14 +86,6 @@ __device__ __forceinline__ float adam_one(float& p, float g, float& m, float& v,
     return p;
 }
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ float4 ld_nt(const float4* p) {
-    const f32x4 v = __builtin_nontemporal_load((const f32x4*)p);
-    return make_float4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ void st_nt(float4* p, float4 v) {
-    __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, (f32x4*)p);
-}
 
 __global__ __launch_bounds__(OPT_THREADS) void adamw_kernel(float4* __restrict__ p, float4* __restrict__ g,
                                                             float4* __restrict__ m, float4* __restrict__ v,
@@ -80,10 +93,10 @@ __global__ __launch_bounds__(OPT_THREADS) void adamw_kernel(float4* __restrict__
                                                             int64_t n_decay4, AdamwDev a,
                                                             const float* __restrict__ scale_ptr) {
     const float sc = scale_ptr[0];
-    for (int64_t i = blockIdx.x * (int64_t)OPT_THREADS + threadIdx.x; i < n4; i += (int64_t)gridDim.x * OPT_THREADS) {
-        // streaming: each element is touched once per step, so the loads and
-        // stores carry the non-temporal hint
-        float4 pp = ld_nt(p + i), gg = ld_nt(g + i), mm = ld_nt(m + i), vv = ld_nt(v + i);
+    // streaming: each element is touched once per step, so the loads and stores
+    // carry the non-temporal hint.  Two vectors per thread per pass, all eight
+    // loads issued before the arithmetic, keep more bytes in flight per thread.
+    auto update = [&](int64_t i, float4 pp, float4 gg, float4 mm, float4 vv) {
         const bool dec = i < n_decay4;
         const float wd = dec ? a.wd : 0.0f;
         adam_one(pp.x, gg.x * sc, mm.x, vv.x, wd, a);
@@ -95,7 +108,17 @@ __global__ __launch_bounds__(OPT_THREADS) void adamw_kernel(float4* __restrict__
         st_nt(v + i, vv);
         st_nt(g + i, make_float4(0.f, 0.f, 0.f, 0.f));
         if (dec && shadow) shadow[i] = make_uint2(pack_bf2(pp.x, pp.y), pack_bf2(pp.z, pp.w));
+    };
+    const int64_t step = (int64_t)gridDim.x * OPT_THREADS;
+    int64_t i = blockIdx.x * (int64_t)OPT_THREADS + threadIdx.x;
+    for (; i + step < n4; i += 2 * step) {
+        const int64_t k = i + step;
+        const float4 p0 = ld_nt(p + i), g0 = ld_nt(g + i), m0 = ld_nt(m + i), v0 = ld_nt(v + i);
+        const float4 p1 = ld_nt(p + k), g1 = ld_nt(g + k), m1 = ld_nt(m + k), v1 = ld_nt(v + k);
+        update(i, p0, g0, m0, v0);
+        update(k, p1, g1, m1, v1);
     }
+    if (i < n4) update(i, ld_nt(p + i), ld_nt(g + i), ld_nt(m + i), ld_nt(v + i));
 }
 
 __global__ __launch_bounds__(OPT_THREADS) void cast_bf16_kernel(const float4* __restrict__ src,
