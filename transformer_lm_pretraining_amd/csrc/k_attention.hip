@@ -36,15 +36,25 @@ constexpr float RESCALE_LOG2 = 8.0f;  // forward: largest probability 2^8 before
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
-// Row block of a workgroup, 0 = the heaviest.  Workgroups reach the eight XCDs
-// round-robin by linear index; with a 1-D grid whose index runs over the B*H
-// heads fastest and the row blocks in order of decreasing causal work, every
-// XCD receives an equal share of each work level (a 2-D grid with the row
-// block fastest would send all of one row block to one XCD).
-__device__ __forceinline__ int attn_unit(int BH, int& bh) {
-    bh = (int)(blockIdx.x % (unsigned)BH);
-    return (int)(blockIdx.x / (unsigned)BH);
+// Work unit of a workgroup: head bh and row-block rank (0 = the heaviest).
+// Workgroups reach the eight XCDs round-robin by linear index (XCD = index mod
+// 8), and each XCD has its own L2.  Head bh goes to XCD bh mod 8, so every row
+// block of a head reads that head's operands through one L2; within an XCD the
+// units run in rank order, the heaviest row block of each of its heads first, so
+// every XCD receives an equal share of each causal work level and the row blocks
+// of one head that run at the same time share their streamed blocks in L2.  The
+// grid holds 8 * ceil(BH / 8) * nunits workgroups; the spare ones of XCDs with a
+// head fewer return false (before any memory access or barrier).
+__device__ __forceinline__ bool attn_unit(int BH, int nunits, int& bh, int& rank) {
+    const int x = (int)(blockIdx.x & 7u), j = (int)(blockIdx.x >> 3);
+    const int nx = (BH - x + 7) >> 3;  // heads x, x + 8, ... below BH
+    if (j >= nx * nunits) return false;
+    rank = j / nx;
+    bh = x + 8 * (j - rank * nx);
+    return true;
 }
+
+inline unsigned attn_grid(int BH, int T) { return (unsigned)(8 * cdiv(BH, 8) * cdiv(T, QB)); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -123,9 +133,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     constexpr int KK = D / 16, DT = D / 32;
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][KVB * LD];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][KVB * LD];
-    int bh;
-    const int nqb = (int)(gridDim.x / (unsigned)BH);
-    const int q0 = (nqb - 1 - attn_unit(BH, bh)) * QB;  // heaviest blocks first
+    const int nqb = (int)cdiv(T, QB);
+    int bh, rank;
+    if (!attn_unit(BH, nqb, bh, rank)) return;
+    const int q0 = (nqb - 1 - rank) * QB;  // heaviest blocks first
     const int b = bh / H, h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: causal tests are scalar branches
@@ -275,8 +286,9 @@ __global__ __launch_bounds__(256, 2) void attn_dkdv_kernel(const uint16_t* __res
     __shared__ __attribute__((aligned(16))) uint16_t sdO[2][KVB * LD];
     __shared__ __attribute__((aligned(16))) float sL[2][KVB];
     __shared__ __attribute__((aligned(16))) float sDv[2][KVB];
-    int bh;
-    const int k0 = attn_unit(BH, bh) * QB;  // the first key blocks see the most queries
+    int bh, rank;
+    if (!attn_unit(BH, (int)cdiv(T, QB), bh, rank)) return;
+    const int k0 = rank * QB;  // the first key blocks see the most queries
     const int b = bh / H, h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: causal tests are scalar branches
@@ -442,9 +454,10 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(const uint16_t* __restr
     constexpr int KK = D / 16, DT = D / 32;
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][KVB * LD];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][KVB * LD];
-    int bh;
-    const int nqb = (int)(gridDim.x / (unsigned)BH);
-    const int q0 = (nqb - 1 - attn_unit(BH, bh)) * QB;
+    const int nqb = (int)cdiv(T, QB);
+    int bh, rank;
+    if (!attn_unit(BH, nqb, bh, rank)) return;
+    const int q0 = (nqb - 1 - rank) * QB;
     const int b = bh / H, h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: causal tests are scalar branches
@@ -583,7 +596,7 @@ double attn_work(int B, int T, int H, int D, int matmuls) {
 template <int D>
 hipError_t fwd_t(const uint16_t* qkv, uint16_t* out, float* lse, int B, int T, int H, int C, hipStream_t s) {
     const float sl = LOG2E / sqrtf((float)D);
-    dim3 grid((unsigned)(cdiv(T, QB) * B * H));
+    dim3 grid(attn_grid(B * H, T));
     PROF_LAUNCH(KC_ATTN_FWD, attn_work(B, T, H, D, 2), s,
                 hipLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(256), 0, s, qkv, out, lse, T, H, C, B * H, sl));
     return hipGetLastError();
@@ -594,7 +607,7 @@ hipError_t bwd_t(const uint16_t* qkv, const uint16_t* out, const uint16_t* dout,
                  float* dvec, int B, int T, int H, int C, hipStream_t s) {
     const float scale = 1.0f / sqrtf((float)D);
     const float scale_log2 = LOG2E * scale;
-    dim3 grid((unsigned)(cdiv(T, QB) * B * H));
+    dim3 grid(attn_grid(B * H, T));
     PROF_LAUNCH(KC_ATTN_DQ, attn_work(B, T, H, D, 3), s,
                 hipLaunchKernelGGL(attn_dq_kernel<D>, grid, dim3(256), 0, s, qkv, out, dout, lse, dvec, dqkv, T, H, C,
                                    B * H, scale_log2, scale));
