@@ -4,6 +4,11 @@
     python -m transformer_lm_pretraining_amd.profile_summary counters --a A.csv --b B.csv \
         --fetch FETCH.csv --write WRITE.csv --copy-fetch CF.csv --copy-write CW.csv
     python -m transformer_lm_pretraining_amd.profile_summary block KERNEL_TRACE.csv --layers 12
+    python -m transformer_lm_pretraining_amd.profile_summary grid KERNEL_TRACE.csv
+    python -m transformer_lm_pretraining_amd.profile_summary ntclass [KERNEL_TRACE.csv] [--fetch F.csv --write W.csv
+        --copy-fetch CF.csv --copy-write CW.csv] [model sizes]
+    python -m transformer_lm_pretraining_amd.profile_summary hbm KERNEL_TRACE.csv [--fetch F.csv --write W.csv
+        --copy-fetch CF.csv --copy-write CW.csv] [model sizes]
 
 stats: per-kernel calls, average and total duration from a --kernel-trace --stats run.
 counters: per kernel (and grid size) from --pmc runs: MFMA-busy fraction of the SIMD
@@ -15,6 +20,15 @@ block: time of one transformer block's kernels per micro-step, taken from the di
   sequence of a step trace (the block kernels between the embedding and the final
   LayerNorm in the forward, and between the final LayerNorm's backward and the grouped
   weight-gradient launch in the backward), plus 1/L of the weight-gradient launches.
+grid: calls, average and total duration per kernel and grid size, from the kernel trace.
+ntclass: the dominant kernel class (NT GEMMs with a bf16 output: gemm_nt_w8_kernel<0> and <5>) per
+  micro-step: its launches by grid size, time, the FLOP of its 6L + 2 products (sum of 2MNK from the model
+  sizes) and the fraction of the 2.5 PF bf16 peak; with counter files (--fetch, --write, --copy-fetch,
+  --copy-write; the trace may be omitted) its HBM bytes per launch against the algorithmic bytes.
+hbm: the memory-bound kernels' average duration, algorithmic bytes (from the model sizes), achieved TB/s
+  against 8 TB/s, and with counter files the HBM bytes they moved (FETCH_SIZE and WRITE_SIZE scaled by a
+  plain copy's readings).
+Model sizes: --layers L --c C --bt B*T --t T --vp padded vocabulary (defaults: GPT-2 124M at 19 x 1024).
 """
 from __future__ import annotations
 
@@ -117,6 +131,128 @@ def cmd_block(path: str, layers: int) -> None:
           "launches %.1f us, total %.1f us" % (n, sum(blocks) / n, sum(dw) / n, (sum(blocks) + sum(dw)) / n))
 
 
+def trace_rows(path: str):
+    return sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+
+
+def by_grid(path: str):
+    """{(kernel, grid): [durations in us]} over the trace"""
+    d = collections.defaultdict(list)
+    for r in trace_rows(path):
+        d[(short(r["Kernel_Name"]), int(r["Grid_Size_X"]))].append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return d
+
+
+def cmd_grid(path: str, top: int) -> None:
+    d = by_grid(path)
+    print("%-44s %10s %6s %10s %10s" % ("kernel", "grid", "calls", "avg_us", "total_ms"))
+    for k in sorted(d, key=lambda k: -sum(d[k]))[:top]:
+        v = d[k]
+        print("%-44s %10d %6d %10.2f %10.2f" % (k[0][:44], k[1], len(v), sum(v) / len(v), sum(v) / 1e3))
+
+
+NT_CLASS = ("gemm_nt_w8_kernel<0,", "gemm_nt_w8_kernel<5,")
+PEAK_BF16 = 2.5e15
+
+
+def nt_products(L: int, C: int, BT: int, Vp: int):
+    """(name, M, N, K) of the class's products in one micro-step"""
+    per_layer = [("QKV", BT, 3 * C, C), ("attention projection + residual", BT, C, C),
+                 ("FC-proj + residual", BT, C, 4 * C), ("FC input gradient", BT, C, 4 * C),
+                 ("attention-projection input gradient", BT, C, C), ("QKV input gradient", BT, C, 3 * C)]
+    return per_layer * L + [("lm_head forward", BT, Vp, C), ("lm_head input gradient", BT, C, Vp)]
+
+
+def nt_traffic(fetch, write, cfetch, cwrite, L, C, BT, Vp) -> None:
+    """HBM bytes per launch of the class from counter runs, against its algorithmic bytes"""
+    F, W = per_dispatch(fetch), per_dispatch(write)
+    fs = (1 << 20) / copy_kib(cfetch, "FETCH_SIZE")
+    ws = (1 << 20) / copy_kib(cwrite, "WRITE_SIZE")
+    cls = [k for k in F if k[0].startswith(NT_CLASS)]
+    n = sum(F[k]["_n"] for k in cls)
+    fk = sum(F[k]["FETCH_SIZE"] * F[k]["_n"] for k in cls) / n
+    wk = sum(W[k]["WRITE_SIZE"] * W[k]["_n"] for k in cls) / n
+    rd, wr = fk * 1024 * fs / 1e6, wk * 1024 * ws / 1e6
+    res = ("attention projection + residual", "FC-proj + residual")
+    prods = nt_products(L, C, BT, Vp)
+    # A + B + output (+ residual input), bf16
+    alg = sum(2 * (m * k + n_ * k + m * n_) + (2 * m * n_ if nm in res else 0) for nm, m, n_, k in prods) / len(prods) / 1e6
+    print("copy calibration: FETCH_SIZE x %.5f, WRITE_SIZE x %.5f" % (fs, ws))
+    print("counter traffic over %d dispatches: FETCH_SIZE avg %.2f KiB -> %.1f MB read, WRITE_SIZE avg %.2f KiB -> "
+          "%.1f MB written per launch" % (n, fk, rd, wk, wr))
+    print("traffic %.1f MB per launch; algorithmic %.1f MB per launch (A + B + output [+ residual], bf16, averaged "
+          "over the %d products); ratio %.2f" % (rd + wr, alg, len(prods), (rd + wr) / alg))
+    print("by grid (MB read / written per launch):")
+    for k in sorted(cls, key=lambda k: k[1]):
+        print("  %-44s %10d %9.1f / %8.1f" % (k[0][:44], k[1], F[k]["FETCH_SIZE"] * 1024 * fs / 1e6,
+                                             W[k]["WRITE_SIZE"] * 1024 * ws / 1e6))
+
+
+def cmd_ntclass(path: str, L: int, C: int, BT: int, Vp: int) -> None:
+    d = by_grid(path)
+    micro = sum(len(v) for k, v in d.items() if k[0].startswith("xent_kernel"))
+    cls = {k: v for k, v in d.items() if k[0].startswith(NT_CLASS)}
+    prods = nt_products(L, C, BT, Vp)
+    flop = sum(2.0 * m * n * k for _, m, n, k in prods)
+    print("micro-steps in the trace: %d; class launches per micro-step: %d" % (micro, len(prods)))
+    print("%-44s %10s %6s %10s %12s" % ("kernel", "grid", "calls", "avg_us", "per_micro_us"))
+    tot = 0.0
+    for k in sorted(cls, key=lambda k: -sum(cls[k])):
+        v = cls[k]
+        tot += sum(v)
+        print("%-44s %10d %6d %10.2f %12.1f" % (k[0][:44], k[1], len(v), sum(v) / len(v), sum(v) / micro))
+    t_micro = tot / micro
+    print("time per micro-step %.1f us over %d launches = %.2f us per launch" % (t_micro, len(prods), t_micro / len(prods)))
+    print("work per micro-step %.1f GFLOP (%.2f GFLOP per launch) -> %.1f TFLOP/s = %.3f of 2.5 PF" % (
+        flop / 1e9, flop / len(prods) / 1e9, flop / (t_micro * 1e-6) / 1e12, flop / (t_micro * 1e-6) / PEAK_BF16))
+
+
+def mem_kernels(L: int, C: int, BT: int, T: int, Vp: int):
+    """(kernel prefix, label, algorithmic bytes per launch)"""
+    n_decay = Vp * C + T * C + L * 12 * C * C
+    n_params = n_decay + L * 13 * C + 2 * C
+    return [("xent_kernel", "CE: logits read, dz written in place", 4 * BT * Vp),
+            ("ln_fwd16_kernel", "LayerNorm fwd: R x, W y, W mean/rstd", 4 * BT * C + 8 * BT),
+            ("ln_bwd_kernel", "LayerNorm bwd: R x, dy, dres, mean/rstd, W dx", 8 * BT * C + 8 * BT),
+            ("adamw_kernel", "AdamW: R p,g,m,v; W p,m,v; zero g; W shadow", 32 * n_params + 2 * n_decay),
+            ("sumsq_kernel", "global norm: R grads", 4 * n_params),
+            ("transpose_batch_kernel", "transposed bf16 weight copies, R + W", 4 * (Vp * C + 12 * L * C * C)),
+            ("embedding_fwd_kernel", "embedding fwd: R wte rows, wpe rows, W x0", 4 * BT * C + 2 * T * C)]
+
+
+def cmd_hbm(path, fetch, write, cfetch, cwrite, L, C, BT, T, Vp) -> None:
+    d = by_grid(path)
+    F = per_dispatch(fetch) if fetch else {}
+    W = per_dispatch(write) if write else {}
+    fs = (1 << 20) / copy_kib(cfetch, "FETCH_SIZE") if cfetch else None
+    ws = (1 << 20) / copy_kib(cwrite, "WRITE_SIZE") if cwrite else None
+    if fs and ws:
+        print("copy calibration: FETCH_SIZE x %.5f, WRITE_SIZE x %.5f" % (fs, ws))
+    print("%-18s %-46s %9s %9s %6s %6s %10s" % ("kernel", "algorithmic bytes", "MB", "avg_us", "TB/s", "of 8", "counter MB"))
+    for pre, label, nbytes in mem_kernels(L, C, BT, T, Vp):
+        ks = [k for k in d if k[0].startswith(pre)]
+        if not ks:
+            continue
+        v = [x for k in ks for x in d[k]]
+        us = sum(v) / len(v)
+        cnt = ""
+        fk = [k for k in F if k[0].startswith(pre)]
+        wk = [k for k in W if k[0].startswith(pre)]
+        if fs and ws and fk and wk:
+            cnt = "%.1f" % ((F[fk[0]]["FETCH_SIZE"] * fs + W[wk[0]]["WRITE_SIZE"] * ws) * 1024 / 1e6)
+        print("%-18s %-46s %9.1f %9.2f %6.2f %6.3f %10s" % (pre.replace("_kernel", ""), label[:46], nbytes / 1e6, us,
+                                                          nbytes / (us * 1e-6) / 1e12, nbytes / (us * 1e-6) / 8e12, cnt))
+
+
+def model_args(p) -> None:
+    p.add_argument("--layers", type=int, default=12)
+    p.add_argument("--c", type=int, default=768)
+    p.add_argument("--bt", type=int, default=19456)
+    p.add_argument("--t", type=int, default=1024)
+    p.add_argument("--vp", type=int, default=50304)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -130,13 +266,35 @@ def main(argv=None):
     bl = sub.add_parser("block")
     bl.add_argument("path")
     bl.add_argument("--layers", type=int, default=12)
+    g = sub.add_parser("grid")
+    g.add_argument("path")
+    g.add_argument("--top", type=int, default=40)
+    n = sub.add_parser("ntclass")
+    n.add_argument("path", nargs="?")
+    for k in ("fetch", "write", "copy_fetch", "copy_write"):
+        n.add_argument("--" + k.replace("_", "-"))
+    model_args(n)
+    h = sub.add_parser("hbm")
+    h.add_argument("path")
+    for k in ("fetch", "write", "copy_fetch", "copy_write"):
+        h.add_argument("--" + k.replace("_", "-"))
+    model_args(h)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         cmd_stats(a.path, a.top)
     elif a.cmd == "counters":
         cmd_counters(a.a, a.b, a.fetch, a.write, a.copy_fetch, a.copy_write, a.top)
-    else:
+    elif a.cmd == "block":
         cmd_block(a.path, a.layers)
+    elif a.cmd == "grid":
+        cmd_grid(a.path, a.top)
+    elif a.cmd == "ntclass":
+        if a.path:
+            cmd_ntclass(a.path, a.layers, a.c, a.bt, a.vp)
+        if a.fetch:
+            nt_traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.layers, a.c, a.bt, a.vp)
+    else:
+        cmd_hbm(a.path, a.fetch, a.write, a.copy_fetch, a.copy_write, a.layers, a.c, a.bt, a.t, a.vp)
 
 
 if __name__ == "__main__":
