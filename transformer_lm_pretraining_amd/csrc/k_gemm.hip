@@ -363,7 +363,10 @@ __device__ __forceinline__ void wait_stage_groups(int n) {
 // reduction columns (rows of 2*KD bytes; 128-byte rows make every L2 request
 // a full line), NS stages in LDS.  The 16-byte vector c of a row r sits at
 // slot c ^ swz(r) so the fragment reads of 16 consecutive rows hit distinct
-// bank groups.  Waits, barrier placement and epilogue as in the 4-wave kernel.
+// bank groups.  At the end of each stage every wave waits for its own loads of
+// the next stage, one barrier makes all of them visible, and the buffer just
+// read takes the stage after next; the epilogue stages the bf16 tile through
+// LDS and stores 16-byte row segments.
 template <int KD>
 struct NtStage {
     static constexpr int CPR = KD / 8;                // 16-byte vectors per row

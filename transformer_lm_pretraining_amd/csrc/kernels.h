@@ -78,7 +78,7 @@ int64_t embedding_bwd_work_elems(int64_t rows, int V, int C);
 hipError_t launch_embedding_bwd(const int32_t* tok, const uint16_t* dx, float* dwte, float* dwpe, int B, int T,
                                 int C, int V, int32_t* work, int64_t work_elems, hipStream_t s);
 
-// ---- attention (k_attn.hip) --------------------------------------------------
+// ---- attention (k_attention.hip) ---------------------------------------------
 hipError_t launch_attention_fwd(const uint16_t* qkv, uint16_t* out, float* lse, int B, int T, int H, int C,
                                 hipStream_t s);
 hipError_t launch_attention_bwd(const uint16_t* qkv, const uint16_t* out, const uint16_t* dout, const float* lse,

@@ -24,10 +24,10 @@ extern thread_local ProfSink* g_prof_sink;
 
 // Kernel class ids (one compiled kernel each).
 enum KernelClass {
-    KC_GEMM_NT = 1,        // gemm_kernel NT, bf16 epilogue (bias / residual)
-    KC_GEMM_NT_GELU = 2,   // gemm_kernel NT, bias + GELU epilogue
-    KC_GEMM_TN_ACC = 3,    // gemm_kernel TN, fp32 += epilogue
-    KC_GEMM_TN_SPLIT = 4,  // gemm_kernel TN, fp32 split-K partials
+    KC_GEMM_NT = 1,        // NT GEMM (gemm_nt_w8_kernel; gemm_kernel below 128 tiles), bf16 epilogue (bias / residual)
+    KC_GEMM_NT_GELU = 2,   // NT GEMM, bias + GELU epilogue
+    KC_GEMM_TN_ACC = 3,    // TN GEMM (gemm_tn_w8_kernel; gemm_kernel for small shapes), fp32 += epilogue
+    KC_GEMM_TN_SPLIT = 4,  // TN GEMM, fp32 split-K partials
     KC_SPLITK_REDUCE = 5,
     KC_ATTN_FWD = 6,
     KC_ATTN_DVEC = 7,      // reserved: D = rowsum(dO * O) is taken inside the dQ kernel
@@ -48,7 +48,7 @@ enum KernelClass {
     KC_TRANSPOSE = 22,
     KC_MEAN = 23,
     KC_BIAS_GELU_FWD = 24,
-    KC_GEMM_NT_DGELU = 25, // gemm_kernel NT, output times GELU'(pre) epilogue
+    KC_GEMM_NT_DGELU = 25, // NT GEMM, output times GELU'(pre) epilogue
     KC_OTHER = 26,
     KC_COUNT = 27
 };
