@@ -292,131 +292,151 @@ __global__ __launch_bounds__(256) void embedding_fwd_kernel(const int32_t* __res
 }
 
 // Token-table gradient, with every addition in a fixed order (the same bits on
-// every run).  (1) The rows are counting-sorted by token id in one workgroup
-// (count, scan and scatter in LDS); the scan also leaves each token's bucket
-// start in global memory.  (2) Within each bucket the rows are put in
-// increasing row order (a row's place is the number of smaller row ids in its
-// bucket).  (3) Each wave sums a window of EMB_WIN sorted rows run by run, for a
-// chunk of columns.  A run inside one window is the only writer of its table
-// row and read-modify-writes it; the pieces of a run that crosses window edges
-// go to per-window scratch (H: the window's first run, T: its last run).
-// (4) One pass adds each crossing run's pieces, window by window, into its
-// table row.  A token occurring N times (Zipf: the most frequent id covers ~14%
-// of a batch) costs about N / EMB_WIN additions to its table row.  Ids outside
-// [0, V) are left out.
+// every run).  (1) The rows with a valid id are sorted by token with a stable
+// two-pass LSD radix sort (8 bits of the 16-bit id per pass), so the rows of
+// each token come out in increasing row order.  (2) Each wave sums a window of
+// EMB_WIN sorted rows run by run, for a chunk of columns.  A run inside one
+// window is the only writer of its table row and read-modify-writes it; the
+// pieces of a run that crosses window edges go to per-window scratch (H: the
+// window's first run, T: its last run).  (3) One pass adds each crossing run's
+// pieces, window by window, into its table row.  A token occurring N times
+// (Zipf: the most frequent id covers ~14% of a batch) costs about N / EMB_WIN
+// additions to its table row.  Ids outside [0, V) are left out.
 constexpr int EMB_WIN = 32;
 
-// Counting sort of the row ids by token in one workgroup, all in LDS: 16-bit
-// counts packed two per word (a chunk has fewer than 65,536 rows), counted with
-// LDS atomics, scanned in place into start offsets (also written to bstart[0..V],
-// bstart[V] = number of valid rows), then advanced by the scatter.  Writes
-// order[] / stok[] (row index and token of each sorted position; the order
-// within a bucket is not yet fixed) and the valid row count to *nvalid.
-constexpr int EMB_SORT_THREADS = 1024;
-__global__ __launch_bounds__(EMB_SORT_THREADS) void emb_sort_kernel(const int32_t* __restrict__ tok, int rows, int V,
-                                                                    int32_t* __restrict__ order,
-                                                                    int32_t* __restrict__ stok,
-                                                                    int32_t* __restrict__ bstart,
-                                                                    int32_t* __restrict__ nvalid) {
-    __shared__ uint32_t cnt[32768];  // counts of token t in half (t & 1) of word t >> 1
-    __shared__ int wtot[EMB_SORT_THREADS / 64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int words = (V + 1) >> 1;
-    for (int i = tid; i < words; i += EMB_SORT_THREADS) cnt[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < rows; i += EMB_SORT_THREADS) {
+// Radix sort: EMB_SORT_ROWS consecutive input positions per workgroup (one per
+// thread).  Pass P orders by bits [8P, 8P + 8) of the id.  hist[d * nb + b]
+// holds how many keys of block b have digit d, so its exclusive scan in that
+// order is where block b's keys of digit d start.
+constexpr int EMB_SORT_ROWS = 1024;
+constexpr int EMB_SORT_WAVES = EMB_SORT_ROWS / 64;
+
+// Input position i of pass P: pass 0 reads row i of the token ids (valid when
+// the id is in [0, V)); pass 1 reads position i of pass 0's output (valid below
+// the number of valid rows).
+template <int P>
+__device__ __forceinline__ bool emb_key(const int32_t* __restrict__ tok, int n, int V,
+                                        const int32_t* __restrict__ in_key, int nv, int i, int& key) {
+    key = 0;
+    if (P == 0) {
+        if (i >= n) return false;
         const int t = tok[i];
-        if (t >= 0 && t < V) atomicAdd(&cnt[t >> 1], 1u << ((t & 1) * 16));
+        if (t < 0 || t >= V) return false;
+        key = t;
+        return true;
     }
-    __syncthreads();
-    // exclusive scan over the counts: thread tid owns words [tid*per, (tid+1)*per)
-    const int per = (words + EMB_SORT_THREADS - 1) / EMB_SORT_THREADS;
-    const int w0 = min(tid * per, words), w1 = min(w0 + per, words);
-    int local = 0;
-    for (int w = w0; w < w1; ++w) local += (int)(cnt[w] & 0xffffu) + (int)(cnt[w] >> 16);
-    int x = local;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, WAVE);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) wtot[wave] = x;
-    __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wave; ++w) before += wtot[w];
-    int run = before + x - local;
-    for (int w = w0; w < w1; ++w) {
-        const uint32_t c = cnt[w];
-        const uint32_t lo = (uint32_t)run, hi = (uint32_t)(run + (int)(c & 0xffffu));
-        run = (int)hi + (int)(c >> 16);
-        cnt[w] = lo | (hi << 16);
-    }
-    if (tid == EMB_SORT_THREADS - 1) {
-        *nvalid = run;
-        bstart[V] = run;
-    }
-    __syncthreads();
-    for (int t = tid; t < V; t += EMB_SORT_THREADS) bstart[t] = (int)((cnt[t >> 1] >> ((t & 1) * 16)) & 0xffffu);
-    __syncthreads();
-    for (int i = tid; i < rows; i += EMB_SORT_THREADS) {
-        const int t = tok[i];
-        if (t < 0 || t >= V) continue;
-        const int sh = (t & 1) * 16;
-        const int pos = (int)((atomicAdd(&cnt[t >> 1], 1u << sh) >> sh) & 0xffffu);
-        order[pos] = i;
-        stok[pos] = t;
-    }
+    if (i >= nv) return false;
+    key = in_key[i];
+    return true;
 }
 
-// Sorted position p of bucket [s, e) takes the row whose id has rank p - s among
-// the bucket's ids (ids in a bucket are distinct), from the scatter's order.  A
-// block of 256 positions copies the ids of every bucket it touches into LDS
-// (EMB_RANK_TILE at a time, all loads in flight); each thread counts the smaller
-// ids inside its own bucket, four per LDS read where the range allows.
-constexpr int EMB_RANK_TILE = 8192;
-__global__ __launch_bounds__(256) void emb_rank_kernel(const int32_t* __restrict__ scattered,
-                                                       const int32_t* __restrict__ stok,
-                                                       const int32_t* __restrict__ bstart,
-                                                       const int32_t* __restrict__ nvalid,
-                                                       int32_t* __restrict__ order) {
-    __shared__ int4 ids4[EMB_RANK_TILE / 4];
-    const int* ids = (const int*)ids4;
-    const int n = *nvalid;
-    const int b0 = blockIdx.x * 256;
-    if (b0 >= n) return;
-    const int b1 = min(b0 + 256, n);
-    const int p = b0 + threadIdx.x;
-    const bool live = p < n;
-    const int t = stok[live ? p : b0];
-    const int s = bstart[t], e = bstart[t + 1];
-    const int my = live ? scattered[p] : 0;
-    const int u0 = bstart[stok[b0]], u1 = bstart[stok[b1 - 1] + 1];  // the buckets this block touches
-    int rank = 0;
-    for (int q0 = u0; q0 < u1; q0 += EMB_RANK_TILE) {
-        const int m = min(EMB_RANK_TILE, u1 - q0);
-        __syncthreads();
-        for (int i = threadIdx.x; i < m; i += 256) ((int*)ids4)[i] = scattered[q0 + i];
-        __syncthreads();
-        int k = max(s - q0, 0);
-        const int k1 = min(e - q0, m);
-        for (; k < k1 && (k & 3); ++k) rank += ids[k] < my ? 1 : 0;
-#pragma unroll 8
-        for (; k + 4 <= k1; k += 4) {
-            const int4 v = ids4[k >> 2];
-            rank += (v.x < my ? 1 : 0) + (v.y < my ? 1 : 0) + (v.z < my ? 1 : 0) + (v.w < my ? 1 : 0);
-        }
-        for (; k < k1; ++k) rank += ids[k] < my ? 1 : 0;
+// The lanes of this wave that hold a valid key with the same 8-bit digit (one
+// ballot per digit bit); rank = how many of them sit in lower lanes.
+__device__ __forceinline__ uint64_t emb_digit_match(int dig, bool valid, int lane, int& rank) {
+    uint64_t m = __ballot(valid);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const bool bit = (dig >> k) & 1;
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
     }
-    if (live) order[s + rank] = my;
+    rank = __popcll(m & ((1ull << lane) - 1ull));
+    return m;
+}
+
+template <int P>
+__global__ __launch_bounds__(EMB_SORT_ROWS) void emb_hist_kernel(const int32_t* __restrict__ tok, int n, int V,
+                                                                 const int32_t* __restrict__ in_key,
+                                                                 const int32_t* __restrict__ nvalid,
+                                                                 int32_t* __restrict__ hist, int nb) {
+    __shared__ int h[256];
+    const int tid = threadIdx.x, lane = tid & 63, b = blockIdx.x;
+    if (tid < 256) h[tid] = 0;
+    __syncthreads();
+    int key;
+    const bool valid = emb_key<P>(tok, n, V, in_key, P == 0 ? 0 : *nvalid, b * EMB_SORT_ROWS + tid, key);
+    const int dig = (key >> (8 * P)) & 255;
+    int rank;
+    const uint64_t m = emb_digit_match(dig, valid, lane, rank);
+    if (valid && rank == 0) atomicAdd(&h[dig], (int)__popcll(m));  // one add per digit and wave
+    __syncthreads();
+    if (tid < 256) hist[tid * nb + b] = h[tid];
+}
+
+// Stable scatter of pass P: a key's place is where its digit starts for this
+// block (scan of hist), plus the keys of that digit in lower waves of the block,
+// plus those in lower lanes of its wave.  Pass 0 also records the number of
+// valid rows; pass 1 writes the sorted tokens and row ids.
+template <int P>
+__global__ __launch_bounds__(EMB_SORT_ROWS) void emb_scatter_kernel(const int32_t* __restrict__ tok, int n, int V,
+                                                                    const int32_t* __restrict__ hist, int nb,
+                                                                    const int32_t* __restrict__ in_key,
+                                                                    const int32_t* __restrict__ in_row,
+                                                                    int32_t* __restrict__ out_key,
+                                                                    int32_t* __restrict__ out_row,
+                                                                    int32_t* __restrict__ nvalid) {
+    __shared__ int off[256];
+    __shared__ int wpre[EMB_SORT_WAVES][256];
+    __shared__ int wsum[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, b = blockIdx.x;
+    for (int i = tid; i < EMB_SORT_WAVES * 256; i += EMB_SORT_ROWS) (&wpre[0][0])[i] = 0;
+    const int nv = P == 0 ? 0 : *nvalid;
+    int before = 0, total = 0, incl = 0;
+    if (tid < 256) {  // digit tid: keys in lower blocks, keys in all blocks, inclusive scan over digits
+        const int32_t* hd = hist + (int64_t)tid * nb;
+        for (int j = 0; j < nb; ++j) {
+            const int c = hd[j];
+            total += c;
+            before += j < b ? c : 0;
+        }
+        incl = total;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o, WAVE);
+            if (lane >= o) incl += y;
+        }
+        if (lane == 63) wsum[wave] = incl;
+    }
+    int key;
+    const int i = b * EMB_SORT_ROWS + tid;
+    const bool valid = emb_key<P>(tok, n, V, in_key, nv, i, key);
+    const int dig = (key >> (8 * P)) & 255;
+    int rank;
+    const uint64_t m = emb_digit_match(dig, valid, lane, rank);
+    __syncthreads();
+    if (tid < 256) {
+        int lower = 0;
+        for (int w = 0; w < wave; ++w) lower += wsum[w];
+        off[tid] = lower + incl - total + before;
+    }
+    if (P == 0 && b == 0 && tid == 0) *nvalid = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    if (valid && rank == 0) wpre[wave][dig] = (int)__popcll(m);
+    __syncthreads();
+    if (tid < 256) {  // exclusive scan over the waves, digit tid
+        int run = 0;
+        for (int w = 0; w < EMB_SORT_WAVES; ++w) {
+            const int c = wpre[w][tid];
+            wpre[w][tid] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    if (!valid) return;
+    const int pos = off[dig] + wpre[wave][dig] + rank;
+    out_key[pos] = key;
+    out_row[pos] = P == 0 ? i : in_row[i];
 }
 
 // One wave per (window of EMB_WIN sorted rows, chunk of 256 columns); each lane
-// owns 4 columns.  part: [window][2][C] floats (H, then T).
+// owns 4 columns.  part: [window][2][C] floats (H, then T).  The column-chunk 0
+// wave also records, for each run that ends in its window, the end position
+// (one past its last sorted row) in bend[token].
 __global__ __launch_bounds__(256) void emb_segsum_kernel(const int32_t* __restrict__ order,
                                                          const int32_t* __restrict__ stok,
                                                          const int32_t* __restrict__ nvalid,
                                                          const uint16_t* __restrict__ dx, int C,
-                                                         float* __restrict__ dwte, float* __restrict__ part) {
+                                                         float* __restrict__ dwte, float* __restrict__ part,
+                                                         int32_t* __restrict__ bend) {
     const int n = *nvalid;
     const int nch = (C / 4 + 63) / 64;
     const int wid = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * 256 + threadIdx.x) >> 6));
@@ -427,6 +447,10 @@ __global__ __launch_bounds__(256) void emb_segsum_kernel(const int32_t* __restri
     const int p1 = min(p0 + EMB_WIN, n);
     const bool head_shared = p0 > 0 && stok[p0 - 1] == stok[p0];
     const bool tail_shared = p1 < n && stok[p1] == stok[p1 - 1];
+    if (ch == 0 && lane < p1 - p0) {  // lane q: does the run at sorted position p0 + q end there?
+        const int p = p0 + lane, t = stok[p];
+        if (p + 1 >= n || stok[p + 1] != t) bend[t] = p + 1;
+    }
     const int c4 = ch * 64 + lane;
     if (c4 >= C / 4) return;
     u32x2 gv[EMB_WIN];
@@ -473,7 +497,7 @@ __global__ __launch_bounds__(256) void emb_segsum_kernel(const int32_t* __restri
 // ends (H; that window holds the bucket's last row), added in window order, then
 // into its table row.  Block (w, y): window w, 64 column vectors of 4.
 __global__ __launch_bounds__(64) void emb_combine_kernel(const int32_t* __restrict__ stok,
-                                                         const int32_t* __restrict__ bstart,
+                                                         const int32_t* __restrict__ bend,
                                                          const int32_t* __restrict__ nvalid, int C,
                                                          const float* __restrict__ part, float* __restrict__ dwte) {
     const int n = *nvalid;
@@ -485,7 +509,7 @@ __global__ __launch_bounds__(64) void emb_combine_kernel(const int32_t* __restri
     const int c4 = blockIdx.y * 64 + threadIdx.x;
     if (c4 >= C / 4) return;
     const int t = stok[p1 - 1];
-    const int wlast = (bstart[t + 1] - 1) / EMB_WIN;
+    const int wlast = (bend[t] - 1) / EMB_WIN;
     float4 acc = *(const float4*)(part + (int64_t)(2 * w + 1) * C + c4 * 4);
     int w2 = w + 1;
     for (; w2 + 8 <= wlast + 1; w2 += 8) {  // eight loads in flight, added in window order
@@ -589,10 +613,13 @@ hipError_t launch_embedding_fwd(const int32_t* tok, const uint16_t* wte, const u
 }
 
 namespace {
-constexpr int64_t EMB_CHUNK = 65535;  // the sort keeps 16-bit offsets: larger batches go in chunks
-// work: nvalid (+ 3 pad), scattered ids, sorted ids, sorted tokens (nmax each), bucket starts
-// (V + 1), then the window pieces (floats) from the next 16-byte boundary
-int64_t emb_part_offset(int64_t nmax, int V) { return (4 + 3 * nmax + V + 1 + 3) / 4 * 4; }
+constexpr int64_t EMB_CHUNK = 65535;  // rows per chunk; larger batches go in several
+// work (int32): nvalid (+ 3 pad), the two histograms (256 x blocks each), pass 0's
+// keys and rows, the sorted tokens and rows (nmax each), bucket ends (V), then
+// the window pieces (floats) from the next 16-byte boundary
+int64_t emb_part_offset(int64_t nmax, int V) {
+    return (4 + 2 * 256 * cdiv(nmax, EMB_SORT_ROWS) + 4 * nmax + V + 3) / 4 * 4;
+}
 }  // namespace
 
 int64_t embedding_bwd_work_elems(int64_t rows, int V, int C) {
@@ -607,25 +634,35 @@ hipError_t launch_embedding_bwd(const int32_t* tok, const uint16_t* dx, float* d
         rows > INT32_MAX)
         return hipErrorInvalidValue;
     const int64_t nmax = std::min(rows, EMB_CHUNK);
+    const int64_t nbmax = cdiv(nmax, EMB_SORT_ROWS);
     int32_t* nvalid = work;
-    int32_t* scattered = work + 4;
-    int32_t* order = scattered + nmax;
-    int32_t* stok = order + nmax;
-    int32_t* bstart = stok + nmax;
+    int32_t* hist0 = work + 4;
+    int32_t* hist1 = hist0 + 256 * nbmax;
+    int32_t* key0 = hist1 + 256 * nbmax;
+    int32_t* row0 = key0 + nmax;
+    int32_t* stok = row0 + nmax;
+    int32_t* order = stok + nmax;
+    int32_t* bend = order + nmax;
     float* part = (float*)(work + emb_part_offset(nmax, V));
     for (int64_t r0 = 0; r0 < rows; r0 += EMB_CHUNK) {
-        const int64_t n = std::min(EMB_CHUNK, rows - r0);
+        const int n = (int)std::min(EMB_CHUNK, rows - r0);
+        const int nb = (int)cdiv(n, EMB_SORT_ROWS);
         const int64_t nwin = cdiv(n, EMB_WIN);
         const int64_t nwaves = nwin * cdiv(C / 4, 64);
+        const int32_t* tk = tok + r0;
         PROF_LAUNCH(KC_EMB_BWD_WTE, 4.0 * n * C + 8.0 * n * C, s, {
-            hipLaunchKernelGGL(emb_sort_kernel, dim3(1), dim3(EMB_SORT_THREADS), 0, s, tok + r0, (int)n, V, scattered,
-                               stok, bstart, nvalid);
-            hipLaunchKernelGGL(emb_rank_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, scattered, stok, bstart,
-                               nvalid, order);
+            hipLaunchKernelGGL(emb_hist_kernel<0>, dim3(nb), dim3(EMB_SORT_ROWS), 0, s, tk, n, V, nullptr, nvalid,
+                               hist0, nb);
+            hipLaunchKernelGGL(emb_scatter_kernel<0>, dim3(nb), dim3(EMB_SORT_ROWS), 0, s, tk, n, V, hist0, nb,
+                               nullptr, nullptr, key0, row0, nvalid);
+            hipLaunchKernelGGL(emb_hist_kernel<1>, dim3(nb), dim3(EMB_SORT_ROWS), 0, s, tk, n, V, key0, nvalid,
+                               hist1, nb);
+            hipLaunchKernelGGL(emb_scatter_kernel<1>, dim3(nb), dim3(EMB_SORT_ROWS), 0, s, tk, n, V, hist1, nb,
+                               key0, row0, stok, order, nvalid);
             hipLaunchKernelGGL(emb_segsum_kernel, dim3((unsigned)cdiv(nwaves, 4)), dim3(256), 0, s, order, stok,
-                               nvalid, dx + r0 * C, C, dwte, part);
+                               nvalid, dx + r0 * C, C, dwte, part, bend);
             hipLaunchKernelGGL(emb_combine_kernel, dim3((unsigned)nwin, (unsigned)cdiv(C / 4, 64)), dim3(64), 0, s,
-                               stok, bstart, nvalid, C, part, dwte);
+                               stok, bend, nvalid, C, part, dwte);
         });
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -72,8 +72,8 @@ hipError_t launch_xent(uint16_t* logits, const int32_t* tgt, float* loss_rows, i
 hipError_t launch_mean(const float* x, const int32_t* tgt, int64_t n, float* out, hipStream_t s);
 hipError_t launch_embedding_fwd(const int32_t* tok, const uint16_t* wte, const uint16_t* wpe, uint16_t* x, int B,
                                 int T, int C, int V, int32_t* flag, hipStream_t s);
-// work: embedding_bwd_work_elems(B*T, V, C) int32 scratch, 16-byte aligned (counting sort of
-// the rows by token, bucket starts, and the pieces of runs that cross summation windows)
+// work: embedding_bwd_work_elems(B*T, V, C) int32 scratch, 16-byte aligned (radix sort of the
+// rows by token, bucket ends, and the pieces of runs that cross summation windows)
 int64_t embedding_bwd_work_elems(int64_t rows, int V, int C);
 hipError_t launch_embedding_bwd(const int32_t* tok, const uint16_t* dx, float* dwte, float* dwpe, int B, int T,
                                 int C, int V, int32_t* work, int64_t work_elems, hipStream_t s);
