@@ -2,6 +2,8 @@
 // gradients (column sums), the fused masked softmax cross-entropy, the
 // embedding lookup and its scatter-add backward.  All move 16-byte vectors
 // (8 bf16) per lane and keep fp32 arithmetic (PDS §4 precision paragraph).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
@@ -242,10 +244,22 @@ __global__ __launch_bounds__(1024) void mean_kernel(const float* __restrict__ x,
     __shared__ double red[16];
     __shared__ double cnt[16];
     double s = 0.0, c = 0.0;
-    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
-        if (tgt && tgt[i] == GPT2_IGNORE_TARGET) continue;
-        s += x[i];
-        c += 1.0;
+    // thread j adds rows j, j + 1024, j + 2048, ... in that order, eight loads in flight
+    for (int64_t i0 = threadIdx.x; i0 < n; i0 += 8 * (int64_t)blockDim.x) {
+        float xv[8];
+        bool ok[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t i = i0 + u * (int64_t)blockDim.x;
+            ok[u] = i < n && (!tgt || tgt[i] != GPT2_IGNORE_TARGET);
+            xv[u] = i < n ? x[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (ok[u]) {
+                s += xv[u];
+                c += 1.0;
+            }
     }
     s = wave_sum_d(s);
     c = wave_sum_d(c);
@@ -531,13 +545,34 @@ __global__ __launch_bounds__(64) void emb_combine_kernel(const int32_t* __restri
     *(float4*)d = o;
 }
 
+// Position-table gradient: each thread owns VEC consecutive entries of the T x C
+// table and adds the batch's B rows of them in batch order (16- or 8-byte loads).
+template <int VEC>
 __global__ __launch_bounds__(256) void embedding_bwd_wpe_kernel(const uint16_t* __restrict__ dx,
                                                                 float* __restrict__ dwpe, int B, int T, int C) {
-    const int64_t total = (int64_t)T * C;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-        float s = 0.f;
-        for (int b = 0; b < B; ++b) s += bf2f(dx[(int64_t)b * total + i]);
-        dwpe[i] += s;
+    using LoadT = std::conditional_t<VEC == 8, u32x4, u32x2>;
+    const int64_t total = (int64_t)T * C, nvec = total / VEC;
+    for (int64_t v = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * blockDim.x) {
+        float s[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s[e] = 0.f;
+        const uint16_t* src = dx + v * VEC;
+#pragma unroll 4
+        for (int b = 0; b < B; ++b) {
+            const LoadT w = *(const LoadT*)(src + (int64_t)b * total);
+#pragma unroll
+            for (int e = 0; e < VEC / 2; ++e) {
+                s[2 * e] += bflo(w[e]);
+                s[2 * e + 1] += bfhi(w[e]);
+            }
+        }
+        float* d = dwpe + v * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+            float4 o = *(float4*)(d + e);
+            o.x += s[e]; o.y += s[e + 1]; o.z += s[e + 2]; o.w += s[e + 3];
+            *(float4*)(d + e) = o;
+        }
     }
 }
 
@@ -667,6 +702,13 @@ hipError_t launch_embedding_bwd(const int32_t* tok, const uint16_t* dx, float* d
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    PROF_LAUNCH(KC_EMB_BWD_WPE, 2.0 * rows * C + 8.0 * T * C, s, hipLaunchKernelGGL(embedding_bwd_wpe_kernel, dim3(grid_for((int64_t)T * C)), dim3(256), 0, s, dx, dwpe, B, T, C));
+    if (((int64_t)T * C) % 8 == 0)
+        PROF_LAUNCH(KC_EMB_BWD_WPE, 2.0 * rows * C + 8.0 * T * C, s,
+                    hipLaunchKernelGGL(embedding_bwd_wpe_kernel<8>, dim3(grid_for((int64_t)T * C / 8)), dim3(256), 0,
+                                       s, dx, dwpe, B, T, C));
+    else  // C % 4 == 0
+        PROF_LAUNCH(KC_EMB_BWD_WPE, 2.0 * rows * C + 8.0 * T * C, s,
+                    hipLaunchKernelGGL(embedding_bwd_wpe_kernel<4>, dim3(grid_for((int64_t)T * C / 4)), dim3(256), 0,
+                                       s, dx, dwpe, B, T, C));
     return hipGetLastError();
 }
