@@ -109,6 +109,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt2_124m", choices=sorted(WORKLOADS))
+    ap.add_argument("--lanes", type=int, default=2,
+                    help="micro-steps in flight at once, each lane on its own stream (1 = all on one stream)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true", help="skip the per-kernel event timing")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -142,7 +144,11 @@ def main():
     torch.cuda.set_device(0)
     cfg = lib.make_config(L, H, C, V, Vp, Tmax, B, T)
     model = lib.GPT2(cfg, seed=1337)
-    n_steps = args.warmup + args.steps + 1
+    nl = max(1, min(args.lanes, n_micro))
+    lanes = [model] + [model.add_lane() for _ in range(nl - 1)]
+    main_stream = torch.cuda.current_stream()
+    streams = [torch.cuda.Stream() for _ in range(nl)] if nl > 1 else [main_stream]
+    n_steps = args.warmup + 1 + args.steps + 5  # warmup, breakdown, timed and roofline steps
     toks = synth.token_stream(n_steps * n_micro * B * T + 1, V)
     data = torch.from_numpy(toks).cuda()  # device-resident before timing
     BT = B * T
@@ -151,13 +157,28 @@ def main():
     losses = torch.zeros(n_micro, dtype=torch.float32, device="cuda")
     t_adam = 350
 
-    def step(i):
+    def step(i, serial=False):
+        """Micro-step k runs on lane k % nl, each lane on its own stream; lane 1 starts once
+        lane 0's first forward is done, so a forward of one lane meets a backward of the other.
+        serial: every micro-step on the main stream (the same lanes, so the same arithmetic)."""
+        st = [main_stream] * nl if serial else streams
+        for x in st:
+            x.wait_stream(main_stream)  # the last update is done
+        first_fwd = torch.cuda.Event()
         for k in range(n_micro):
             base = (i * n_micro + k) * BT
             tok = data[base:base + BT].view(B, T)
             tgt = data[base + 1:base + 1 + BT].view(B, T)
-            model.forward(tok, tgt, dloss=dloss, loss_out=losses[k:k + 1])
-            model.backward()
+            j = k % nl
+            with torch.cuda.stream(st[j]):
+                if k == 1 and nl > 1:
+                    st[1].wait_event(first_fwd)
+                lanes[j].forward(tok, tgt, dloss=dloss, loss_out=losses[k:k + 1])
+                if k == 0 and nl > 1:
+                    first_fwd.record(st[0])
+                lanes[j].backward()
+        for x in st:
+            main_stream.wait_stream(x)
         model.clip_adamw(lr_at(t_adam), t_adam)
 
     say(f"bench: {args.workload} B={B} T={T} x{n_micro} micro-steps; warmup {args.warmup}, timed {args.steps}")
@@ -168,21 +189,32 @@ def main():
 
     names = lib.kernel_class_names()
     breakdown, dominant = {}, None
+    def prof_enable(k):
+        for ln in lanes:
+            ln.prof_enable(k)
+
+    def prof_read(k):
+        tot = [0.0, 0, 0.0]
+        for ln in lanes:
+            for q, x in enumerate(ln.prof_read(k)):
+                tot[q] += x
+        return tot
+
     if not args.no_roofline:
-        model.prof_enable(-1)
-        step(args.warmup)
+        # per-kernel breakdown: one step with every launch timed, its micro-steps one after another
+        prof_enable(-1)
+        step(args.warmup, serial=True)
         for k, n in names.items():
-            ms, cnt, work = model.prof_read(k)
+            ms, cnt, work = prof_read(k)
             if cnt:
                 breakdown[n] = {"ms_per_step": round(ms, 3), "launches": cnt}
-        model.prof_enable(0)
+        prof_enable(0)
         dominant = max(breakdown, key=lambda n: breakdown[n]["ms_per_step"])
         dom_id = [k for k, n in names.items() if n == dominant][0]
         tot = sum(v["ms_per_step"] for v in breakdown.values())
         say("per-kernel ms/step (event-timed): " + ", ".join(
             f"{n} {v['ms_per_step']:.2f}" for n, v in sorted(breakdown.items(), key=lambda x: -x[1]["ms_per_step"])))
         say(f"sum {tot:.1f} ms; dominant kernel: {dominant}")
-        model.prof_enable(dom_id)
 
     first = args.warmup + 1
     torch.cuda.synchronize()
@@ -203,9 +235,21 @@ def main():
 
     roof = None
     if dominant is not None:
+        # The dominant class timed launch by launch on its stream.  With lanes the timed
+        # region overlaps kernels of different lanes, so a launch's duration there is not
+        # the kernel's own; this region runs the next steps of the same workload with the
+        # micro-steps one after another, every launch of the class bracketed by events.
+        n_roof = max(1, min(args.steps, 5))
+        prof_enable(dom_id)
+        torch.cuda.synchronize()
+        r0 = time.perf_counter()
+        for i in range(n_roof):
+            step(first + args.steps + i, serial=True)
+        torch.cuda.synchronize()
+        roof_wall = time.perf_counter() - r0
         traffic = counted_traffic(args.workload, dominant)
-        ms, cnt, work = model.prof_read(dom_id)
-        model.prof_enable(0)
+        ms, cnt, work = prof_read(dom_id)
+        prof_enable(0)
         avg_ms = ms / cnt
         if dominant in lib.MFMA_CLASSES:
             achieved = work / (ms * 1e-3) / 1e12
@@ -218,7 +262,10 @@ def main():
                     "frac": round(achieved / (PEAK_HBM / 1e9), 4), "traffic": traffic,
                     "traffic_unit": "bytes per launch"}
         roof.update({"kernel": dominant, "launches": cnt, "avg_launch_ms": round(avg_ms, 4),
-                     "work_per_launch": work / cnt})
+                     "work_per_launch": work / cnt,
+                     "timing": f"HIP events around every launch of the class on its stream, {n_roof} steps right "
+                               "after the throughput region with the micro-steps in sequence",
+                     "serial_ms_per_step": round(roof_wall * 1e3 / n_roof, 3)})
 
     tps = tokens_per_step * args.steps / wall
     fpt = flop_per_token(L, H, C, V, T)
@@ -239,7 +286,7 @@ def main():
         "config": {"workload": f"{args.workload}: L={L} H={H} C={C} V={V} (padded {Vp}), {B} seq x {T} tok x "
                                f"{n_micro} accumulation micro-steps, clip 1.0 + AdamW at step {t_adam}",
                    "global_batch": tokens_per_step, "seq_len": T, "micro_batch": B, "accum": n_micro,
-                   "parallelism": "single-gpu"},
+                   "parallelism": "single-gpu", "lanes": nl},
         "mfu": round(tps * fpt / PEAK_BF16, 4),
         "flop_per_token": fpt,
         "median_last15_ms": round(med15, 3),

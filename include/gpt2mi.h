@@ -189,13 +189,41 @@ int gpt2_forward(gpt2_handle* h, const int32_t* tok, const int32_t* tgt, float d
 int gpt2_backward(gpt2_handle* h, hipStream_t stream);
 
 /*
+ * Lanes: micro-steps in flight at once.  The n_micro forward/backward pairs
+ * of one accumulated optimizer step (PDS §4.4) depend on each other only
+ * through the gradient sum, so they can run on several streams when each
+ * stream has its own activations and its own gradient accumulator.
+ * gpt2_lane_init creates such a lane of model h: a handle that reads h's
+ * parameters and bf16 shadows (bufs->params, shadow, shadow_t of h) and
+ * writes only `grads` (fp32 [n_params], zeroed here on `stream`), `acts`
+ * (acts_bytes) and `scratch` (scratch_bytes), all caller-owned and 256-byte
+ * aligned.  gpt2_forward / gpt2_backward / gpt2_eval_loss / gpt2_sync_status
+ * and the timing calls take a lane like a model handle; gpt2_clip_adamw does
+ * not (GPT2_E_STATE): it is called on h and takes the gradient as h's
+ * accumulator plus those of its lanes in creation order, then zeroes them all.
+ * Ordering across streams is the caller's: every lane's backward must be
+ * complete before gpt2_clip_adamw(h) starts, and no lane's forward may start
+ * before that call has finished.  At most GPT2_MAX_LANES lanes per model;
+ * a lane cannot have lanes.  Destroy lanes before their model (destroying
+ * the model first detaches them: they keep their buffers but no clip counts
+ * their gradients).  Errors: GPT2_E_INVALID (null/misaligned pointer, h is a
+ * lane), GPT2_E_STATE (GPT2_MAX_LANES lanes exist), GPT2_E_HIP.
+ */
+#define GPT2_MAX_LANES 3
+int gpt2_lane_init(gpt2_handle* h, float* grads, void* acts, void* scratch, hipStream_t stream,
+                   gpt2_handle** lane);
+
+/*
  * Global-norm clip + AdamW over all parameters (PDS §4 optimisation):
  * n = ||grads||_2 (fp32 partial sums, fp64 across blocks); s = min(1,
  * max_norm / n); g = s * grads; m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2;
  * p -= lr * (m/(1-b1^t) / (sqrt(v/(1-b2^t)) + eps) + wd * p), with wd only on
- * the first n_decay elements.  Then refreshes the bf16 shadow (and its
- * transposes) from p and zeroes grads.  Writes n to grad_norm_dev[0] if non-NULL.
- * Errors: GPT2_E_INVALID (t < 1, null args), GPT2_E_HIP.
+ * the first n_decay elements.  grads is the sum of h's accumulator and
+ * those of h's lanes (see gpt2_lane_init), added in that order.  Then
+ * refreshes the bf16 shadow (and its transposes) from p and zeroes every
+ * accumulator.  Writes n to grad_norm_dev[0] if non-NULL.
+ * Errors: GPT2_E_INVALID (t < 1, null args), GPT2_E_STATE (h is a lane),
+ * GPT2_E_HIP.
  */
 int gpt2_clip_adamw(gpt2_handle* h, const gpt2_adamw_args* args, float* grad_norm_dev, hipStream_t stream);
 
@@ -245,7 +273,6 @@ int gpt2_prof_enable(gpt2_handle* h, int32_t kclass);
 int gpt2_prof_read(gpt2_handle* h, hipStream_t stream, int32_t kclass, double* total_ms, int64_t* launches,
                    double* work);
 const char* gpt2_prof_class_name(int32_t kclass);
-
 #ifdef __cplusplus
 }
 #endif

@@ -116,3 +116,10 @@ def test_kernel_entry_points_validate_before_launch(L):
 def test_strerror(L):
     for s in range(7):
         assert L.gpt2_strerror(s)
+
+
+def test_lane_init_validates_without_a_device(L):
+    # a lane needs a model handle and an output pointer
+    lane = ctypes.c_void_p()
+    assert L.gpt2_lane_init(None, 256, 256, 256, None, ctypes.byref(lane)) == lib.GPT2_E_INVALID
+    assert L.gpt2_lane_init(None, 256, 256, 256, None, None) == lib.GPT2_E_INVALID

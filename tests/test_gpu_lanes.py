@@ -1,0 +1,120 @@
+"""Micro-steps in flight on two lanes (gpt2_lane_init): a lane reads its model's
+weights and keeps its own gradient accumulator, so the n_micro forward/backward
+pairs of an accumulated step (PDS §4.4) can run on two streams at once.  The
+step's gradient is the sum over the lanes; it is checked against the oracle's
+gradient of the whole batch, against the one-lane step (same sums in another
+order), and for bitwise repeatability with the lanes' streams overlapping."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.model import CONFIGS, init_params, loss_and_grads
+from transformer_lm_pretraining_amd import synth
+from gpu_util import to_dev_i32, rel_l2, cosine
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _model(cfg, B, T, flat):
+    from transformer_lm_pretraining_amd import lib
+    c = lib.make_config(cfg.L, cfg.H, cfg.C, cfg.V, cfg.Vp, cfg.Tmax, B, T)
+    return lib.GPT2(c, init=flat)
+
+
+def _run(cfg, B, T, flat, batches, lanes, dloss, overlap=True):
+    """One accumulated step; micro-step k on lane k % lanes, each lane on its own stream.
+    Returns (summed grads before the update, params after, norm)."""
+    import torch
+    model = _model(cfg, B, T, flat)
+    ls = [model] + [model.add_lane() for _ in range(lanes - 1)]
+    main = torch.cuda.current_stream()
+    streams = [torch.cuda.Stream() for _ in ls] if overlap else [main] * lanes
+    ids = [(to_dev_i32(tok), to_dev_i32(tgt)) for tok, tgt in batches]  # kept alive until the end
+    for s in streams:
+        s.wait_stream(main)
+    for k, (td, gd) in enumerate(ids):
+        with torch.cuda.stream(streams[k % lanes]):
+            ls[k % lanes].forward(td, gd, dloss=dloss)
+            ls[k % lanes].backward()
+    for s in streams:
+        main.wait_stream(s)
+    g = model.grads.double()
+    for ln in ls[1:]:
+        g = g + ln.grads.double()
+    g_sum = g.cpu().numpy()
+    norm = model.clip_adamw(oracle.lr_at(350), 1)
+    torch.cuda.synchronize()
+    out = (g_sum, model.params.cpu().numpy(), float(norm.item()),
+           [ln.grads.abs().max().item() for ln in ls])
+    return out
+
+
+def test_two_lanes_match_oracle_and_one_lane(gpu_lib):
+    cfg = CONFIGS["tiny"]
+    B, T, n = 4, 64, 4
+    say("lanes: tiny, 4 micro-steps on 2 lanes")
+    P = init_params(cfg, 1337)
+    flat = oracle.flatten(cfg, P)
+    batches = synth.micro_batches(n, B, T, cfg.V, seed=41)
+    dloss = 1.0 / (n * B * T)
+    g2, p2, n2, left = _run(cfg, B, T, flat, batches, 2, dloss)
+    assert max(left) == 0.0, "clip + AdamW zeroes every lane's accumulator"
+    g1, p1, n1, _ = _run(cfg, B, T, flat, batches, 1, dloss)
+    # the oracle's gradient of the whole accumulated batch
+    tok = np.concatenate([b[0] for b in batches])
+    tgt = np.concatenate([b[1] for b in batches])
+    _, G, _ = loss_and_grads(cfg, P, tok, tgt, dloss=dloss, dtype=np.float64)
+    ref = oracle.flatten(cfg, G, dtype=np.float64)
+    r, c = rel_l2(g2, ref), cosine(g2, ref)
+    say("lanes vs oracle: rel L2", r, "cos", c)
+    assert r <= 3e-2 and c >= 0.999
+    # same terms summed in another order: fp32 accumulation differences only
+    assert rel_l2(g2, g1) <= 1e-5, rel_l2(g2, g1)
+    assert abs(n2 - n1) <= 1e-5 * n1
+    upd1, upd2 = p1 - flat, p2 - flat
+    assert rel_l2(upd2, upd1) <= 1e-3, rel_l2(upd2, upd1)
+
+
+def test_two_lanes_bitwise_repeatable(gpu_lib):
+    """Overlapping lanes give the same bits on every run: each lane's sums have a fixed
+    order and the update adds the lanes' accumulators in creation order."""
+    from oracle.model import Config
+    cfg = Config(L=2, H=12, C=768, V=50257, Vp=50304, Tmax=1024)
+    B, T, n = 2, 1024, 4
+    say("lanes: bitwise repeat, 2 layers of 124M shape, 4 micro-steps")
+    flat = oracle.flatten(cfg, init_params(cfg, 1337))
+    batches = synth.micro_batches(n, B, T, cfg.V, seed=43)
+    a = _run(cfg, B, T, flat, batches, 2, 1.0 / (n * B * T))
+    b = _run(cfg, B, T, flat, batches, 2, 1.0 / (n * B * T))
+    assert np.array_equal(a[0], b[0]), int(np.sum(a[0] != b[0]))
+    assert np.array_equal(a[1], b[1]) and a[2] == b[2]
+
+
+def test_lane_call_order(gpu_lib):
+    import torch
+    from transformer_lm_pretraining_amd import lib
+    cfg = CONFIGS["tiny"]
+    flat = oracle.flatten(cfg, init_params(cfg, 1337))
+    model = _model(cfg, 2, 64, flat)
+    lanes = [model.add_lane() for _ in range(3)]
+    with pytest.raises(lib.Gpt2Error) as ei:
+        model.add_lane()
+    assert ei.value.status == lib.GPT2_E_STATE
+    a = lib.AdamwArgs(1e-4, 0.9, 0.95, 1e-8, 0.1, 1.0, 1)
+    assert model.lib.gpt2_clip_adamw(lanes[0].h, a, None, lib._stream()) == lib.GPT2_E_STATE
+    import ctypes
+    h = ctypes.c_void_p()
+    assert model.lib.gpt2_lane_init(lanes[0].h, lib._ptr(lanes[1].grads), lib._ptr(lanes[1].acts),
+                                    lib._ptr(lanes[1].scratch), lib._stream(), ctypes.byref(h)) == lib.GPT2_E_INVALID
+    # a closed lane no longer counts: a new one can take its place
+    lanes[2].close()
+    model.lanes.remove(lanes[2])
+    model.add_lane()
+    torch.cuda.synchronize()

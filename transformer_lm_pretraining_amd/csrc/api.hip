@@ -6,6 +6,7 @@
 // optimizer state, statistics and loss.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -216,6 +217,10 @@ struct gpt2_handle {
     ActsPlan acts;
     ScratchPlan scr;
     int64_t n_params, n_decay;
+    // lanes: a lane reads its model's parameters and shadows and owns its grads, acts and scratch
+    bool is_lane = false;
+    gpt2_handle* parent = nullptr;  // null once the model is destroyed
+    std::vector<gpt2_handle*> lanes;
     int last_hip = 0;
     bool grad_ready = false;
     const int32_t* last_tok = nullptr;
@@ -559,8 +564,41 @@ int gpt2_backward(gpt2_handle* h, hipStream_t s) {
     return run_backward(h, s);
 }
 
+int gpt2_lane_init(gpt2_handle* h, float* grads, void* acts, void* scratch, hipStream_t s, gpt2_handle** out) {
+    if (!out) return GPT2_E_INVALID;
+    *out = nullptr;
+    if (!h || h->is_lane || !grads || !acts || !scratch || !aligned(grads) || !aligned(acts) || !aligned(scratch))
+        return GPT2_E_INVALID;
+    if ((int)h->lanes.size() >= GPT2_MAX_LANES) return GPT2_E_STATE;
+    gpt2_handle* l = new gpt2_handle();
+    l->cfg = h->cfg;
+    l->bufs = h->bufs;
+    l->bufs.grads = grads;
+    l->bufs.acts = acts;
+    l->bufs.scratch = scratch;
+    l->tens = h->tens;
+    l->acts = h->acts;
+    l->scr = h->scr;
+    l->n_params = h->n_params;
+    l->n_decay = h->n_decay;
+    l->is_lane = true;
+    l->parent = h;
+    hipError_t e = launch_fill_f32(grads, 0.0f, l->n_params, s);
+    if (e == hipSuccess) e = hipMemsetAsync(scratch, 0, 256, s);
+    if (e != hipSuccess) {
+        h->last_hip = (int)e;
+        delete l;
+        return GPT2_E_HIP;
+    }
+    l->sink.h = l;
+    h->lanes.push_back(l);
+    *out = l;
+    return GPT2_OK;
+}
+
 int gpt2_clip_adamw(gpt2_handle* h, const gpt2_adamw_args* a, float* grad_norm_dev, hipStream_t s) {
     if (!h || !a || a->t < 1 || !(a->max_norm > 0.0f)) return GPT2_E_INVALID;
+    if (h->is_lane) return GPT2_E_STATE;
     SinkGuard guard(h);
     AdamwHostArgs ha;
     ha.lr = a->lr;
@@ -571,8 +609,12 @@ int gpt2_clip_adamw(gpt2_handle* h, const gpt2_adamw_args* a, float* grad_norm_d
     ha.max_norm = a->max_norm;
     ha.inv_bc1 = (float)(1.0 / (1.0 - std::pow((double)a->beta1, (double)a->t)));
     ha.inv_bc2 = (float)(1.0 / (1.0 - std::pow((double)a->beta2, (double)a->t)));
-    HIPCHK(launch_clip_adamw(h->bufs.params, h->bufs.grads, h->bufs.m, h->bufs.v, h->bufs.shadow, h->n_params,
-                             h->n_decay, ha, grad_norm_dev, (double*)(h->S() + h->scr.norm_partial),
+    float* g[GPT2_MAX_LANES + 1];
+    int ng = 0;
+    g[ng++] = h->bufs.grads;
+    for (gpt2_handle* l : h->lanes) g[ng++] = l->bufs.grads;
+    HIPCHK(launch_clip_adamw(h->bufs.params, g, ng, h->bufs.m, h->bufs.v, h->bufs.shadow, h->n_params, h->n_decay, ha,
+                             grad_norm_dev, (double*)(h->S() + h->scr.norm_partial),
                              (float*)(h->S() + h->scr.scale), s));
     return refresh_shadow(h, s);
 }
@@ -614,6 +656,11 @@ int gpt2_last_hip_error(const gpt2_handle* h) { return h ? h->last_hip : 0; }
 
 void gpt2_destroy(gpt2_handle* h) {
     if (!h) return;
+    if (h->parent) {
+        auto& v = h->parent->lanes;
+        v.erase(std::remove(v.begin(), v.end(), h), v.end());
+    }
+    for (gpt2_handle* l : h->lanes) l->parent = nullptr;
     for (auto e : h->ev0) (void)hipEventDestroy(e);  // nothing to report from a destructor
     for (auto e : h->ev1) (void)hipEventDestroy(e);
     delete h;

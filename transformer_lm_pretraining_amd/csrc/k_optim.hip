@@ -22,9 +22,29 @@ __device__ __forceinline__ void st_nt(float4* p, float4 v) {
     __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, (f32x4*)p);
 }
 
+// The gradient is the sum of NG accumulators (the model's and its lanes'),
+// added in accumulator order; element i of it as a vector.
+template <int NG>
+struct GradSum {
+    float4* g[NG];
+    __device__ __forceinline__ float4 at(int64_t i) const {
+        float4 v = ld_nt(g[0] + i);
+#pragma unroll
+        for (int j = 1; j < NG; ++j) {
+            const float4 w = ld_nt(g[j] + i);
+            v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+        }
+        return v;
+    }
+    __device__ __forceinline__ void zero(int64_t i) const {
+#pragma unroll
+        for (int j = 0; j < NG; ++j) st_nt(g[j] + i, make_float4(0.f, 0.f, 0.f, 0.f));
+    }
+};
+
 // Per-block sum of squares of g (fp32 per thread, fp64 across the block).
-__global__ __launch_bounds__(OPT_THREADS) void sumsq_kernel(const float4* __restrict__ g, int64_t n4,
-                                                            double* __restrict__ partial) {
+template <int NG>
+__global__ __launch_bounds__(OPT_THREADS) void sumsq_kernel(GradSum<NG> G, int64_t n4, double* __restrict__ partial) {
     __shared__ double red[OPT_THREADS / 64];
     // four vectors per thread in flight, each in its own accumulator (a fixed order:
     // the same inputs give the same bits)
@@ -34,12 +54,12 @@ __global__ __launch_bounds__(OPT_THREADS) void sumsq_kernel(const float4* __rest
     for (; i + 3 * step < n4; i += 4 * step) {
         float4 v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = g[i + u * step];
+        for (int u = 0; u < 4; ++u) v[u] = G.at(i + u * step);
 #pragma unroll
         for (int u = 0; u < 4; ++u) s4[u] += v[u].x * v[u].x + v[u].y * v[u].y + v[u].z * v[u].z + v[u].w * v[u].w;
     }
     for (; i < n4; i += step) {
-        const float4 v = g[i];
+        const float4 v = G.at(i);
         s4[0] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
     }
     const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
@@ -87,15 +107,16 @@ __device__ __forceinline__ float adam_one(float& p, float g, float& m, float& v,
 }
 
 
-__global__ __launch_bounds__(OPT_THREADS) void adamw_kernel(float4* __restrict__ p, float4* __restrict__ g,
+template <int NG>
+__global__ __launch_bounds__(OPT_THREADS) void adamw_kernel(float4* __restrict__ p, GradSum<NG> G,
                                                             float4* __restrict__ m, float4* __restrict__ v,
                                                             uint2* __restrict__ shadow, int64_t n4,
                                                             int64_t n_decay4, AdamwDev a,
                                                             const float* __restrict__ scale_ptr) {
     const float sc = scale_ptr[0];
     // streaming: each element is touched once per step, so the loads and stores
-    // carry the non-temporal hint.  Two vectors per thread per pass, all eight
-    // loads issued before the arithmetic, keep more bytes in flight per thread.
+    // carry the non-temporal hint.  Two vectors per thread per pass, all loads
+    // issued before the arithmetic, keep more bytes in flight per thread.
     auto update = [&](int64_t i, float4 pp, float4 gg, float4 mm, float4 vv) {
         const bool dec = i < n_decay4;
         const float wd = dec ? a.wd : 0.0f;
@@ -106,19 +127,19 @@ __global__ __launch_bounds__(OPT_THREADS) void adamw_kernel(float4* __restrict__
         st_nt(p + i, pp);
         st_nt(m + i, mm);
         st_nt(v + i, vv);
-        st_nt(g + i, make_float4(0.f, 0.f, 0.f, 0.f));
+        G.zero(i);
         if (dec && shadow) shadow[i] = make_uint2(pack_bf2(pp.x, pp.y), pack_bf2(pp.z, pp.w));
     };
     const int64_t step = (int64_t)gridDim.x * OPT_THREADS;
     int64_t i = blockIdx.x * (int64_t)OPT_THREADS + threadIdx.x;
     for (; i + step < n4; i += 2 * step) {
         const int64_t k = i + step;
-        const float4 p0 = ld_nt(p + i), g0 = ld_nt(g + i), m0 = ld_nt(m + i), v0 = ld_nt(v + i);
-        const float4 p1 = ld_nt(p + k), g1 = ld_nt(g + k), m1 = ld_nt(m + k), v1 = ld_nt(v + k);
+        const float4 p0 = ld_nt(p + i), g0 = G.at(i), m0 = ld_nt(m + i), v0 = ld_nt(v + i);
+        const float4 p1 = ld_nt(p + k), g1 = G.at(k), m1 = ld_nt(m + k), v1 = ld_nt(v + k);
         update(i, p0, g0, m0, v0);
         update(k, p1, g1, m1, v1);
     }
-    if (i < n4) update(i, ld_nt(p + i), ld_nt(g + i), ld_nt(m + i), ld_nt(v + i));
+    if (i < n4) update(i, ld_nt(p + i), G.at(i), ld_nt(m + i), ld_nt(v + i));
 }
 
 __global__ __launch_bounds__(OPT_THREADS) void cast_bf16_kernel(const float4* __restrict__ src,
@@ -228,11 +249,14 @@ int grid_for(int64_t n, int cap = 4096) { return (int)std::max<int64_t>(1, std::
 
 int64_t adamw_partial_elems(int64_t) { return NORM_BLOCKS; }
 
-hipError_t launch_clip_adamw(float* p, float* g, float* m, float* v, uint16_t* shadow, int64_t n, int64_t n_decay,
-                             const AdamwHostArgs& a, float* norm_dev, double* partial, float* scale_dev,
-                             hipStream_t s) {
+namespace {
+template <int NG>
+hipError_t clip_adamw_ng(float* p, float* const* g, float* m, float* v, uint16_t* shadow, int64_t n, int64_t n_decay,
+                         const AdamwHostArgs& a, float* norm_dev, double* partial, float* scale_dev, hipStream_t s) {
     const int64_t n4 = n / 4;
-    PROF_LAUNCH(KC_SUMSQ, 4.0 * n, s, hipLaunchKernelGGL(sumsq_kernel, dim3(NORM_BLOCKS), dim3(OPT_THREADS), 0, s, (const float4*)g, n4, partial));
+    GradSum<NG> G;
+    for (int j = 0; j < NG; ++j) G.g[j] = (float4*)g[j];
+    PROF_LAUNCH(KC_SUMSQ, 4.0 * NG * n, s, hipLaunchKernelGGL(sumsq_kernel<NG>, dim3(NORM_BLOCKS), dim3(OPT_THREADS), 0, s, G, n4, partial));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     PROF_LAUNCH(KC_NORM_FINAL, 8.0 * NORM_BLOCKS, s, hipLaunchKernelGGL(norm_finalize_kernel, dim3(1), dim3(OPT_THREADS), 0, s, partial, NORM_BLOCKS, a.max_norm,
@@ -240,9 +264,29 @@ hipError_t launch_clip_adamw(float* p, float* g, float* m, float* v, uint16_t* s
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     AdamwDev d{a.lr, a.beta1, a.beta2, a.eps, a.wd, a.inv_bc1, a.inv_bc2};
-    PROF_LAUNCH(KC_ADAMW, 32.0 * n + 2.0 * n_decay, s, hipLaunchKernelGGL(adamw_kernel, dim3(grid_for(n4, 8192)), dim3(OPT_THREADS), 0, s, (float4*)p, (float4*)g,
+    PROF_LAUNCH(KC_ADAMW, (24.0 + 8.0 * NG) * n + 2.0 * n_decay, s, hipLaunchKernelGGL(adamw_kernel<NG>, dim3(grid_for(n4, 8192)), dim3(OPT_THREADS), 0, s, (float4*)p, G,
                        (float4*)m, (float4*)v, (uint2*)shadow, n4, n_decay / 4, d, (const float*)scale_dev));
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_clip_adamw(float* p, float* const* g, int ng, float* m, float* v, uint16_t* shadow, int64_t n,
+                             int64_t n_decay, const AdamwHostArgs& a, float* norm_dev, double* partial,
+                             float* scale_dev, hipStream_t s) {
+    switch (ng) {
+        case 1: return clip_adamw_ng<1>(p, g, m, v, shadow, n, n_decay, a, norm_dev, partial, scale_dev, s);
+        case 2: return clip_adamw_ng<2>(p, g, m, v, shadow, n, n_decay, a, norm_dev, partial, scale_dev, s);
+        case 3: return clip_adamw_ng<3>(p, g, m, v, shadow, n, n_decay, a, norm_dev, partial, scale_dev, s);
+        case 4: return clip_adamw_ng<4>(p, g, m, v, shadow, n, n_decay, a, norm_dev, partial, scale_dev, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_clip_adamw(float* p, float* g, float* m, float* v, uint16_t* shadow, int64_t n, int64_t n_decay,
+                             const AdamwHostArgs& a, float* norm_dev, double* partial, float* scale_dev,
+                             hipStream_t s) {
+    float* gs[1] = {g};
+    return launch_clip_adamw(p, gs, 1, m, v, shadow, n, n_decay, a, norm_dev, partial, scale_dev, s);
 }
 
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {

@@ -93,6 +93,11 @@ struct AdamwHostArgs {
 hipError_t launch_clip_adamw(float* p, float* g, float* m, float* v, uint16_t* shadow, int64_t n, int64_t n_decay,
                              const AdamwHostArgs& a, float* norm_dev, double* partial, float* scale_dev,
                              hipStream_t s);
+// The same with the gradient taken as g[0] + ... + g[ng-1] (1 <= ng <= 4, added in that
+// order); every g[j] is zeroed.
+hipError_t launch_clip_adamw(float* p, float* const* g, int ng, float* m, float* v, uint16_t* shadow, int64_t n,
+                             int64_t n_decay, const AdamwHostArgs& a, float* norm_dev, double* partial,
+                             float* scale_dev, hipStream_t s);
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 // dst[c][r] = src[r][c] for a bf16 [R, Cc] matrix.
 hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int R, int Cc, hipStream_t s);

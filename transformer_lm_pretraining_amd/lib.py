@@ -60,6 +60,7 @@ _SIGS = {
     "gpt2_init": (c_int32, [POINTER(Config), c_uint64, c_void_p, POINTER(Buffers), c_void_p, POINTER(c_void_p)]),
     "gpt2_forward": (c_int32, [c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p]),
     "gpt2_backward": (c_int32, [c_void_p, c_void_p]),
+    "gpt2_lane_init": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, POINTER(c_void_p)]),
     "gpt2_clip_adamw": (c_int32, [c_void_p, POINTER(AdamwArgs), c_void_p, c_void_p]),
     "gpt2_eval_loss": (c_int32, [c_void_p, c_void_p, c_void_p, POINTER(c_float), c_void_p]),
     "gpt2_sync_status": (c_int32, [c_void_p, c_void_p]),
@@ -153,47 +154,14 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-class GPT2:
-    """A model instance: caller-owned device buffers (torch) + the library handle."""
-
-    def __init__(self, cfg: Config, seed: int = 1337, init=None, device="cuda"):
-        import torch
-        self.lib = load()
-        self.cfg = cfg
-        self.sz = sizes(cfg)
-        self.table = tensor_table(cfg)
-        dev = torch.device(device)
-        f32 = dict(dtype=torch.float32, device=dev)
-        n = self.sz.n_params
-        self.params = torch.empty(n, **f32)
-        self.grads = torch.empty(n, **f32)
-        self.m = torch.empty(n, **f32)
-        self.v = torch.empty(n, **f32)
-        self.shadow = torch.empty(self.sz.n_decay, dtype=torch.bfloat16, device=dev)
-        self.shadow_t = torch.empty(self.sz.n_shadow_t, dtype=torch.bfloat16, device=dev)
-        self.acts = torch.empty(self.sz.acts_bytes, dtype=torch.uint8, device=dev)
-        self.scratch = torch.empty(self.sz.scratch_bytes, dtype=torch.uint8, device=dev)
-        self.loss_dev = torch.zeros(1, **f32)
-        self.norm_dev = torch.zeros(1, **f32)
-        bufs = Buffers(*[t.data_ptr() for t in (self.params, self.grads, self.m, self.v, self.shadow, self.shadow_t,
-                                                self.acts, self.scratch)])
-        host = None
-        if init is not None:
-            host_arr = np.ascontiguousarray(init, dtype=np.float32)
-            assert host_arr.size == n
-            host = host_arr.ctypes.data_as(c_void_p)
-        h = c_void_p()
-        check(self.lib.gpt2_init(ctypes.byref(cfg), seed, host, ctypes.byref(bufs), _stream(), ctypes.byref(h)),
-              "gpt2_init")
-        self.h = h
-        self._keep = None
+class _Pass:
+    """Forward / backward / evaluation and timing calls shared by a model and its lanes."""
 
     def __del__(self):
         if getattr(self, "h", None):
             self.lib.gpt2_destroy(self.h)
             self.h = None
 
-    # -- the step
     def forward(self, tok, tgt=None, dloss=None, loss_out=None):
         """tok, tgt: int32 device tensors [B, T].  Returns the device loss tensor (mean over B*T) or None."""
         if dloss is None:
@@ -206,13 +174,6 @@ class GPT2:
 
     def backward(self):
         check(self.lib.gpt2_backward(self.h, _stream()), "gpt2_backward")
-
-    def clip_adamw(self, lr, t, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0, norm_out=None):
-        """norm_out: optional fp32 device scalar for the pre-clip norm (default: the model's own)."""
-        a = AdamwArgs(lr, beta1, beta2, eps, weight_decay, max_norm, t)
-        out = norm_out if norm_out is not None else self.norm_dev
-        check(self.lib.gpt2_clip_adamw(self.h, ctypes.byref(a), _ptr(out), _stream()), "gpt2_clip_adamw")
-        return out
 
     def eval_loss(self, tok, tgt) -> float:
         out = c_float()
@@ -260,6 +221,88 @@ class GPT2:
         check(self.lib.gpt2_prof_read(self.h, _stream(), kclass, ctypes.byref(ms), ctypes.byref(n),
                                       ctypes.byref(work)), "gpt2_prof_read")
         return ms.value, n.value, work.value
+
+
+class GPT2(_Pass):
+    """A model instance: caller-owned device buffers (torch) + the library handle."""
+
+    def __init__(self, cfg: Config, seed: int = 1337, init=None, device="cuda"):
+        import torch
+        self.lib = load()
+        self.cfg = cfg
+        self.sz = sizes(cfg)
+        self.table = tensor_table(cfg)
+        dev = torch.device(device)
+        f32 = dict(dtype=torch.float32, device=dev)
+        n = self.sz.n_params
+        self.params = torch.empty(n, **f32)
+        self.grads = torch.empty(n, **f32)
+        self.m = torch.empty(n, **f32)
+        self.v = torch.empty(n, **f32)
+        self.shadow = torch.empty(self.sz.n_decay, dtype=torch.bfloat16, device=dev)
+        self.shadow_t = torch.empty(self.sz.n_shadow_t, dtype=torch.bfloat16, device=dev)
+        self.acts = torch.empty(self.sz.acts_bytes, dtype=torch.uint8, device=dev)
+        self.scratch = torch.empty(self.sz.scratch_bytes, dtype=torch.uint8, device=dev)
+        self.loss_dev = torch.zeros(1, **f32)
+        self.norm_dev = torch.zeros(1, **f32)
+        bufs = Buffers(*[t.data_ptr() for t in (self.params, self.grads, self.m, self.v, self.shadow, self.shadow_t,
+                                                self.acts, self.scratch)])
+        host = None
+        if init is not None:
+            host_arr = np.ascontiguousarray(init, dtype=np.float32)
+            assert host_arr.size == n
+            host = host_arr.ctypes.data_as(c_void_p)
+        h = c_void_p()
+        check(self.lib.gpt2_init(ctypes.byref(cfg), seed, host, ctypes.byref(bufs), _stream(), ctypes.byref(h)),
+              "gpt2_init")
+        self.h = h
+        self._keep = None
+        self.lanes = []
+
+    def __del__(self):
+        for ln in getattr(self, "lanes", []):  # lanes go before their model
+            ln.close()
+        super().__del__()
+
+    def add_lane(self):
+        """A lane of this model (gpt2_lane_init): its own gradient accumulator, activations and scratch."""
+        ln = Lane(self)
+        self.lanes.append(ln)
+        return ln
+
+    def clip_adamw(self, lr, t, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0, norm_out=None):
+        """norm_out: optional fp32 device scalar for the pre-clip norm (default: the model's own).
+        The gradient is the sum of the model's and its lanes' accumulators."""
+        a = AdamwArgs(lr, beta1, beta2, eps, weight_decay, max_norm, t)
+        out = norm_out if norm_out is not None else self.norm_dev
+        check(self.lib.gpt2_clip_adamw(self.h, ctypes.byref(a), _ptr(out), _stream()), "gpt2_clip_adamw")
+        return out
+
+
+class Lane(_Pass):
+    """A lane of a model: reads the model's parameters and shadows, owns grads, acts and scratch."""
+
+    def __init__(self, model: GPT2):
+        import torch
+        self.lib = model.lib
+        self.cfg = model.cfg
+        self.sz = model.sz
+        self.table = model.table
+        dev = model.params.device
+        self.grads = torch.empty(self.sz.n_params, dtype=torch.float32, device=dev)
+        self.acts = torch.empty(self.sz.acts_bytes, dtype=torch.uint8, device=dev)
+        self.scratch = torch.empty(self.sz.scratch_bytes, dtype=torch.uint8, device=dev)
+        self.loss_dev = torch.zeros(1, dtype=torch.float32, device=dev)
+        h = c_void_p()
+        check(self.lib.gpt2_lane_init(model.h, _ptr(self.grads), _ptr(self.acts), _ptr(self.scratch), _stream(),
+                                      ctypes.byref(h)), "gpt2_lane_init")
+        self.h = h
+        self._keep = None
+
+    def close(self):
+        if getattr(self, "h", None):
+            self.lib.gpt2_destroy(self.h)
+            self.h = None
 
 
 def kernel_class_names():

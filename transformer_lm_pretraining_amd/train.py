@@ -66,13 +66,15 @@ class Trainer:
     step late, so the loop never waits on the GPU except to log."""
 
     def __init__(self, workload: str = "gpt2_124m", seed: int = 1337, data_seed: int = 1,
-                 eval_seed: int = 2, device: str = "cuda", init=None):
-        """init: optional host fp32 flat parameters in place of the seeded initialisation."""
+                 eval_seed: int = 2, device: str = "cuda", init=None, lanes: int = 2):
+        """init: optional host fp32 flat parameters in place of the seeded initialisation.
+        lanes: micro-steps in flight at once (gpt2_lane_init), each lane on its own stream."""
         L, H, C, V, Vp, Tmax, B, T, n_micro = WORKLOADS[workload]
         self.workload, self.seed, self.eval_seed = workload, seed, eval_seed
         self.B, self.T, self.V, self.n_micro = B, T, V, n_micro
         self.cfg = lib.make_config(L, H, C, V, Vp, Tmax, B, T)
         self.model = lib.GPT2(self.cfg, seed=seed, init=init, device=device)
+        self.lanes = [self.model] + [self.model.add_lane() for _ in range(max(1, min(lanes, n_micro)) - 1)]
         self.data = synth.TokenStream(V, data_seed)
         self.step = 0  # completed optimizer steps
         self._setup(device)
@@ -91,6 +93,8 @@ class Trainer:
         self._cursor = None  # stream state before those ids were drawn
         self._last_end = None
         self._eval = None
+        nl = len(self.lanes)
+        self._streams = [torch.cuda.Stream(device=self.device) for _ in range(nl)] if nl > 1 else None
 
     def _fill(self, slot):
         """Draws the next step's n_micro micro-batches into staging slot `slot`."""
@@ -117,9 +121,30 @@ class Trainer:
         self._copied[slot] = ev
         m = self.model
         dloss = 1.0 / (self.B * self.T * self.n_micro)
-        for k in range(self.n_micro):
-            m.forward(self._batch[k, 0], self._batch[k, 1], dloss=dloss, loss_out=self._loss[slot, k:k + 1])
-            m.backward()
+        if self._streams is None:
+            for k in range(self.n_micro):
+                m.forward(self._batch[k, 0], self._batch[k, 1], dloss=dloss, loss_out=self._loss[slot, k:k + 1])
+                m.backward()
+        else:
+            # micro-step k on lane k % lanes, each on its own stream behind the ids' copy;
+            # lane 1 starts once lane 0's first forward is done
+            main = torch.cuda.current_stream()
+            for st in self._streams:
+                st.wait_stream(main)
+            first_fwd = torch.cuda.Event()
+            nl = len(self.lanes)
+            for k in range(self.n_micro):
+                j = k % nl
+                with torch.cuda.stream(self._streams[j]):
+                    if k == 1:
+                        self._streams[1].wait_event(first_fwd)
+                    self.lanes[j].forward(self._batch[k, 0], self._batch[k, 1], dloss=dloss,
+                                          loss_out=self._loss[slot, k:k + 1])
+                    if k == 0:
+                        first_fwd.record(self._streams[0])
+                    self.lanes[j].backward()
+            for st in self._streams:
+                main.wait_stream(st)
         lr = lr_at(self.step + 1)
         m.clip_adamw(lr, self.step + 1, norm_out=self._norm[slot:slot + 1])
         end = torch.cuda.Event(enable_timing=True)
@@ -178,7 +203,7 @@ class Trainer:
             np.save(os.path.join(tmp, key + ".npy"), t.detach().cpu().numpy())
         cursor = self._cursor if self._ready else self.data.state()  # ids drawn ahead are drawn again
         meta = {"step": self.step, "workload": self.workload, "seed": self.seed, "eval_seed": self.eval_seed,
-                "data": cursor}
+                "lanes": len(self.lanes), "data": cursor}
         with open(os.path.join(tmp, "meta.json"), "w") as f:
             json.dump(meta, f)
         shutil.rmtree(final, ignore_errors=True)
@@ -204,6 +229,8 @@ class Trainer:
         tr.cfg = lib.make_config(L, H, C, V, Vp, Tmax, B, T)
         params = np.load(os.path.join(ck, "params.npy"))
         tr.model = lib.GPT2(tr.cfg, seed=meta["seed"], init=params, device=device)  # shadows from params
+        # the same lanes as the saved run: the order of the gradient sums, and so the bits, follow them
+        tr.lanes = [tr.model] + [tr.model.add_lane() for _ in range(int(meta.get("lanes", 1)) - 1)]
         for key, t in (("m", tr.model.m), ("v", tr.model.v)):
             t.copy_(torch.from_numpy(np.load(os.path.join(ck, key + ".npy"))).to(t.device))
         tr.data = synth.TokenStream.from_state(meta["data"])
@@ -268,6 +295,7 @@ def main(argv=None):
     ap.add_argument("--eval-batches", type=int, default=EVAL_BATCHES)
     ap.add_argument("--ckpt-every", type=int, default=CKPT_EVERY)
     ap.add_argument("--seed", type=int, default=1337)
+    ap.add_argument("--lanes", type=int, default=2, help="micro-steps in flight at once, each on its own stream")
     ap.add_argument("--supervise", action="store_true", help="run the trainer under the relaunching supervisor")
     ap.add_argument("--max-restarts", type=int, default=10)
     ap.add_argument("--fail-at-step", type=int, default=0,
@@ -292,7 +320,7 @@ def main(argv=None):
         tr = Trainer.resume(a.run_dir)
         print(f"resumed at step {tr.step}", flush=True)
     else:
-        tr = Trainer(a.workload, seed=a.seed)
+        tr = Trainer(a.workload, seed=a.seed, lanes=a.lanes)
     fail = 0 if resumed else a.fail_at_step
     ok = tr.run(a.run_dir, a.steps, a.eval_every, a.eval_batches, a.ckpt_every,
                 log=lambda s: print(s, flush=True), fail_at_step=fail)
