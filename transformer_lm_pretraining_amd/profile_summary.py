@@ -5,6 +5,7 @@
         --fetch FETCH.csv --write WRITE.csv --copy-fetch CF.csv --copy-write CW.csv
     python -m transformer_lm_pretraining_amd.profile_summary block KERNEL_TRACE.csv --layers 12
     python -m transformer_lm_pretraining_amd.profile_summary grid KERNEL_TRACE.csv
+    python -m transformer_lm_pretraining_amd.profile_summary timeline KERNEL_TRACE.csv --first 2 --last 3
     python -m transformer_lm_pretraining_amd.profile_summary ntclass [KERNEL_TRACE.csv] [--fetch F.csv --write W.csv
         --copy-fetch CF.csv --copy-write CW.csv] [model sizes]
     python -m transformer_lm_pretraining_amd.profile_summary hbm KERNEL_TRACE.csv [--fetch F.csv --write W.csv
@@ -25,6 +26,10 @@ ntclass: the dominant kernel class (NT GEMMs with a bf16 output: gemm_nt_w8_kern
   micro-step: its launches by grid size, time, the FLOP of its 6L + 2 products (sum of 2MNK from the model
   sizes) and the fraction of the 2.5 PF bf16 peak; with counter files (--fetch, --write, --copy-fetch,
   --copy-write; the trace may be omitted) its HBM bytes per launch against the algorithmic bytes.
+timeline: for a range of optimizer steps of a step trace (a step ends at its AdamW launch): the step
+  time, the share of it during which the GPU ran at least one kernel and at least two at once, and per
+  kernel the calls, average duration, summed duration and active time (the union of its launches'
+  intervals; launches of different lanes may overlap).
 hbm: the memory-bound kernels' average duration, algorithmic bytes (from the model sizes), achieved TB/s
   against 8 TB/s, and with counter files the HBM bytes they moved (FETCH_SIZE and WRITE_SIZE scaled by a
   plain copy's readings).
@@ -135,10 +140,20 @@ def trace_rows(path: str):
     return sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
 
 
-def by_grid(path: str):
-    """{(kernel, grid): [durations in us]} over the trace"""
+def rows_in_steps(path: str, first=None, last=None):
+    """The trace's dispatches, or those of optimizer steps first..last (0-based, inclusive)."""
+    rows = trace_rows(path)
+    if first is None:
+        return rows
+    win = step_windows(rows)
+    t0, t1 = win[first][0], win[last][1]
+    return [r for r in rows if int(r["Start_Timestamp"]) >= t0 and int(r["End_Timestamp"]) <= t1]
+
+
+def by_grid(path: str, first=None, last=None):
+    """{(kernel, grid): [durations in us]} over the trace (or steps first..last of it)"""
     d = collections.defaultdict(list)
-    for r in trace_rows(path):
+    for r in rows_in_steps(path, first, last):
         d[(short(r["Kernel_Name"]), int(r["Grid_Size_X"]))].append(
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     return d
@@ -150,6 +165,64 @@ def cmd_grid(path: str, top: int) -> None:
     for k in sorted(d, key=lambda k: -sum(d[k]))[:top]:
         v = d[k]
         print("%-44s %10d %6d %10.2f %10.2f" % (k[0][:44], k[1], len(v), sum(v) / len(v), sum(v) / 1e3))
+
+
+def step_windows(rows):
+    """[(start_ns, end_ns)] of the optimizer steps in a trace: a step ends with its AdamW launch
+    and starts where the previous one ended (the first at the first dispatch)."""
+    ends = [int(r["End_Timestamp"]) for r in rows if short(r["Kernel_Name"]).startswith("adamw_kernel")]
+    starts = [int(rows[0]["Start_Timestamp"])] + ends[:-1]
+    return list(zip(starts, ends))
+
+
+def cmd_timeline(path: str, first: int, last: int, top: int) -> None:
+    """Steps first..last (0-based, in dispatch order) of a step trace: wall time, the time the
+    GPU ran at least one kernel and at least two at once, and per kernel the calls, average
+    duration and the time at least one of its launches ran (the union of their intervals)."""
+    rows = trace_rows(path)
+    win = step_windows(rows)
+    t0, t1 = win[first][0], win[last][1]
+    sel = [r for r in rows if int(r["Start_Timestamp"]) >= t0 and int(r["End_Timestamp"]) <= t1]
+    ev = []
+    for r in sel:
+        ev.append((int(r["Start_Timestamp"]), 1))
+        ev.append((int(r["End_Timestamp"]), -1))
+    ev.sort()
+    busy = two = 0
+    level, prev = 0, t0
+    for t, d in ev:
+        if level >= 1:
+            busy += t - prev
+        if level >= 2:
+            two += t - prev
+        level += d
+        prev = t
+
+    def union(iv):
+        iv.sort()
+        tot, lo, hi = 0, None, None
+        for a, b in iv:
+            if hi is None or a > hi:
+                if hi is not None:
+                    tot += hi - lo
+                lo, hi = a, b
+            else:
+                hi = max(hi, b)
+        return tot + (hi - lo if hi is not None else 0)
+
+    per = collections.defaultdict(list)
+    for r in sel:
+        per[short(r["Kernel_Name"])].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    n = last - first + 1
+    wall = t1 - t0
+    print("steps %d..%d (%d): %.3f ms per step; GPU running >= 1 kernel %.1f%% of the time, >= 2 kernels %.1f%%"
+          % (first, last, n, wall / n / 1e6, 100.0 * busy / wall, 100.0 * two / wall))
+    print("%-44s %7s %10s %14s %14s" % ("kernel", "calls", "avg_us", "sum_ms/step", "active_ms/step"))
+    for k in sorted(per, key=lambda k: -sum(b - a for a, b in per[k]))[:top]:
+        iv = per[k]
+        tot = sum(b - a for a, b in iv)
+        print("%-44s %7d %10.2f %14.2f %14.2f" % (k[:44], len(iv), tot / len(iv) / 1e3, tot / n / 1e6,
+                                                  union(list(iv)) / n / 1e6))
 
 
 NT_CLASS = ("gemm_nt_w8_kernel<0,", "gemm_nt_w8_kernel<5,")
@@ -189,8 +262,10 @@ def nt_traffic(fetch, write, cfetch, cwrite, L, C, BT, Vp) -> None:
                                              W[k]["WRITE_SIZE"] * 1024 * ws / 1e6))
 
 
-def cmd_ntclass(path: str, L: int, C: int, BT: int, Vp: int) -> None:
-    d = by_grid(path)
+def cmd_ntclass(path: str, L: int, C: int, BT: int, Vp: int, first=None, last=None) -> None:
+    d = by_grid(path, first, last)
+    if first is not None:
+        print("optimizer steps %d..%d of the trace" % (first, last))
     micro = sum(len(v) for k, v in d.items() if k[0].startswith("xent_kernel"))
     cls = {k: v for k, v in d.items() if k[0].startswith(NT_CLASS)}
     prods = nt_products(L, C, BT, Vp)
@@ -266,11 +341,18 @@ def main(argv=None):
     bl = sub.add_parser("block")
     bl.add_argument("path")
     bl.add_argument("--layers", type=int, default=12)
+    tl = sub.add_parser("timeline")
+    tl.add_argument("trace")
+    tl.add_argument("--first", type=int, required=True, help="first optimizer step (0-based)")
+    tl.add_argument("--last", type=int, required=True, help="last optimizer step (0-based, inclusive)")
+    tl.add_argument("--top", type=int, default=30)
     g = sub.add_parser("grid")
     g.add_argument("path")
     g.add_argument("--top", type=int, default=40)
     n = sub.add_parser("ntclass")
     n.add_argument("path", nargs="?")
+    n.add_argument("--first", type=int, help="first optimizer step of the trace to count (0-based)")
+    n.add_argument("--last", type=int, help="last optimizer step to count (inclusive)")
     for k in ("fetch", "write", "copy_fetch", "copy_write"):
         n.add_argument("--" + k.replace("_", "-"))
     model_args(n)
@@ -288,9 +370,11 @@ def main(argv=None):
         cmd_block(a.path, a.layers)
     elif a.cmd == "grid":
         cmd_grid(a.path, a.top)
+    elif a.cmd == "timeline":
+        cmd_timeline(a.trace, a.first, a.last, a.top)
     elif a.cmd == "ntclass":
         if a.path:
-            cmd_ntclass(a.path, a.layers, a.c, a.bt, a.vp)
+            cmd_ntclass(a.path, a.layers, a.c, a.bt, a.vp, a.first, a.last)
         if a.fetch:
             nt_traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.layers, a.c, a.bt, a.vp)
     else:
