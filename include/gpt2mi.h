@@ -207,7 +207,8 @@ int gpt2_backward(gpt2_handle* h, hipStream_t stream);
  * a lane cannot have lanes.  Destroy lanes before their model (destroying
  * the model first detaches them: they keep their buffers but no clip counts
  * their gradients).  Errors: GPT2_E_INVALID (null/misaligned pointer, h is a
- * lane), GPT2_E_STATE (GPT2_MAX_LANES lanes exist), GPT2_E_HIP.
+ * lane, a buffer overlapping another of the lane's or any buffer of h or of its
+ * lanes), GPT2_E_STATE (GPT2_MAX_LANES lanes exist), GPT2_E_HIP.
  */
 #define GPT2_MAX_LANES 3
 int gpt2_lane_init(gpt2_handle* h, float* grads, void* acts, void* scratch, hipStream_t stream,

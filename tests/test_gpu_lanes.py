@@ -98,21 +98,34 @@ def test_two_lanes_bitwise_repeatable(gpu_lib):
 
 
 def test_lane_call_order(gpu_lib):
+    import ctypes
     import torch
     from transformer_lm_pretraining_amd import lib
     cfg = CONFIGS["tiny"]
     flat = oracle.flatten(cfg, init_params(cfg, 1337))
     model = _model(cfg, 2, 64, flat)
-    lanes = [model.add_lane() for _ in range(3)]
+    lanes = [model.add_lane() for _ in range(2)]
+    h = ctypes.c_void_p()
+    # buffers shared with the model or another lane, or with each other, are refused
+    fresh = lambda t: torch.empty_like(t)
+    for g, a_, sc in ((model.grads, fresh(model.acts), fresh(model.scratch)),
+                      (lanes[0].grads, fresh(model.acts), fresh(model.scratch)),
+                      (fresh(model.grads), model.acts, fresh(model.scratch)),
+                      (fresh(model.grads), fresh(model.acts), lanes[1].scratch),
+                      (model.params, fresh(model.acts), fresh(model.scratch)),
+                      (model.m[256:], fresh(model.acts), fresh(model.scratch))):
+        assert model.lib.gpt2_lane_init(model.h, lib._ptr(g), lib._ptr(a_), lib._ptr(sc), lib._stream(),
+                                        ctypes.byref(h)) == lib.GPT2_E_INVALID
+    assert not h.value
+    lanes.append(model.add_lane())
     with pytest.raises(lib.Gpt2Error) as ei:
         model.add_lane()
     assert ei.value.status == lib.GPT2_E_STATE
     a = lib.AdamwArgs(1e-4, 0.9, 0.95, 1e-8, 0.1, 1.0, 1)
     assert model.lib.gpt2_clip_adamw(lanes[0].h, a, None, lib._stream()) == lib.GPT2_E_STATE
-    import ctypes
-    h = ctypes.c_void_p()
-    assert model.lib.gpt2_lane_init(lanes[0].h, lib._ptr(lanes[1].grads), lib._ptr(lanes[1].acts),
-                                    lib._ptr(lanes[1].scratch), lib._stream(), ctypes.byref(h)) == lib.GPT2_E_INVALID
+    assert model.lib.gpt2_lane_init(lanes[0].h, lib._ptr(fresh(model.grads)), lib._ptr(fresh(model.acts)),
+                                    lib._ptr(fresh(model.scratch)), lib._stream(),
+                                    ctypes.byref(h)) == lib.GPT2_E_INVALID
     # a closed lane no longer counts: a new one can take its place
     lanes[2].close()
     model.lanes.remove(lanes[2])

@@ -570,6 +570,42 @@ int gpt2_lane_init(gpt2_handle* h, float* grads, void* acts, void* scratch, hipS
     if (!h || h->is_lane || !grads || !acts || !scratch || !aligned(grads) || !aligned(acts) || !aligned(scratch))
         return GPT2_E_INVALID;
     if ((int)h->lanes.size() >= GPT2_MAX_LANES) return GPT2_E_STATE;
+    // the lane's buffers may not overlap the model's or another lane's (shared gradient
+    // accumulators would be counted twice, shared activations or scratch would race)
+    struct Span {
+        const void* p;
+        int64_t n;
+    };
+    auto spans_of = [](const gpt2_handle* x, std::vector<Span>& v) {
+        const int64_t pb = x->n_params * (int64_t)sizeof(float);
+        v.push_back({x->bufs.grads, pb});
+        v.push_back({x->bufs.acts, x->acts.total});
+        v.push_back({x->bufs.scratch, x->scr.total});
+        if (!x->is_lane) {
+            v.push_back({x->bufs.params, pb});
+            v.push_back({x->bufs.m, pb});
+            v.push_back({x->bufs.v, pb});
+            v.push_back({x->bufs.shadow, x->n_decay * (int64_t)sizeof(uint16_t)});
+            int64_t nt = 0;
+            for (const Tensor& t : x->tens)
+                if (t.toff >= 0) nt += t.rows * t.cols;
+            v.push_back({x->bufs.shadow_t, nt * (int64_t)sizeof(uint16_t)});
+        }
+    };
+    std::vector<Span> used;
+    spans_of(h, used);
+    for (const gpt2_handle* x : h->lanes) spans_of(x, used);
+    const Span mine[3] = {{grads, h->n_params * (int64_t)sizeof(float)}, {acts, h->acts.total}, {scratch, h->scr.total}};
+    auto overlap = [](const Span& a, const Span& b) {
+        const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+        return a0 < b0 + (uintptr_t)b.n && b0 < a0 + (uintptr_t)a.n;
+    };
+    for (int i = 0; i < 3; ++i) {
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(mine[i], mine[j])) return GPT2_E_INVALID;
+        for (const Span& u : used)
+            if (overlap(mine[i], u)) return GPT2_E_INVALID;
+    }
     gpt2_handle* l = new gpt2_handle();
     l->cfg = h->cfg;
     l->bufs = h->bufs;
