@@ -39,69 +39,57 @@ __global__ __launch_bounds__(256) void bias_gelu_fwd_kernel(const u32x4* __restr
 }
 
 // Column-sum layout: block b handles rows [b*rpb, (b+1)*rpb); thread t owns the
-// 8-wide column vectors t, t+256, ... and keeps their sums in registers.
-constexpr int CS_THREADS = 256;
-constexpr int CS_MAXV = 4;  // N <= 8 * 256 * 4 = 8192
+// 8-wide column vector t (a block has one thread per vector of a row, rounded up
+// to whole waves) and keeps its sums in registers.  Four rows are loaded before
+// any of them is used, and several blocks run per CU, so enough loads are in
+// flight to stream HBM.  Each block leaves one partial row of column sums;
+// fold_colsum_kernel adds the partial rows in a fixed order.
+constexpr int CS_MAX_THREADS = 1024;  // N <= 8 * 1024 = 8192
+constexpr int CS_ROWS = 4;            // rows in flight per thread
 
-int colsum_blocks(int64_t rows) { return (int)std::min<int64_t>(256, cdiv(rows, 16)); }
+int colsum_blocks(int64_t rows) { return (int)std::min<int64_t>(1024, cdiv(rows, 16)); }
+int colsum_threads(int N) { return (int)std::min<int64_t>(CS_MAX_THREADS, cdiv(N / 8, 64) * 64); }
 
 template <bool GELU_BWD>
-__global__ __launch_bounds__(CS_THREADS) void colsum_kernel(const uint16_t* __restrict__ src, int64_t lds,
-                                                            const uint16_t* __restrict__ pre,
-                                                            uint16_t* __restrict__ dst, float* __restrict__ partial,
-                                                            int64_t rows, int N) {
-    const int nv = N / 8;
+__global__ __launch_bounds__(CS_MAX_THREADS) void colsum_kernel(const uint16_t* __restrict__ src, int64_t lds,
+                                                                const uint16_t* __restrict__ pre,
+                                                                uint16_t* __restrict__ dst,
+                                                                float* __restrict__ partial, int64_t rows, int N) {
+    const int cv = threadIdx.x;
+    if (cv >= N / 8) return;  // no barrier below
     const int64_t rpb = cdiv(rows, gridDim.x);
     const int64_t r0 = blockIdx.x * rpb;
     const int64_t r1 = std::min<int64_t>(rows, r0 + rpb);
-    float acc[CS_MAXV][8];
+    float acc[8];
 #pragma unroll
-    for (int q = 0; q < CS_MAXV; ++q)
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    // rows r .. r+n-1: loads first, then the sums in row order
+    auto rows_at = [&](int64_t r, int n) {
+        u32x4 w[CS_ROWS], pw[CS_ROWS];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
-    int64_t r = r0;
-    if constexpr (!GELU_BWD) {
-        // four rows' loads in flight, added in row order
-        for (; r + 4 <= r1; r += 4) {
-#pragma unroll
-            for (int q = 0; q < CS_MAXV; ++q) {
-                const int cv = threadIdx.x + CS_THREADS * q;
-                if (cv >= nv) break;
-                u32x4 w[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) w[u] = *(const u32x4*)(src + (r + u) * lds + cv * 8);
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        acc[q][2 * e] += bflo(w[u][e]);
-                        acc[q][2 * e + 1] += bfhi(w[u][e]);
-                    }
+        for (int u = 0; u < CS_ROWS; ++u)
+            if (u < n) {
+                w[u] = *(const u32x4*)(src + (r + u) * lds + cv * 8);
+                if constexpr (GELU_BWD) pw[u] = *(const u32x4*)(pre + (r + u) * (int64_t)N + cv * 8);
             }
-        }
-    }
-    for (; r < r1; ++r) {
 #pragma unroll
-        for (int q = 0; q < CS_MAXV; ++q) {
-            const int cv = threadIdx.x + CS_THREADS * q;
-            if (cv >= nv) break;
-            u32x4 w = *(const u32x4*)(src + r * lds + cv * 8);
+        for (int u = 0; u < CS_ROWS; ++u) {
+            if (u >= n) break;
             float x[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                x[2 * e] = bflo(w[e]);
-                x[2 * e + 1] = bfhi(w[e]);
+                x[2 * e] = bflo(w[u][e]);
+                x[2 * e + 1] = bfhi(w[u][e]);
             }
             if constexpr (GELU_BWD) {
-                u32x4 pw = *(const u32x4*)(pre + r * (int64_t)N + cv * 8);
                 u32x4 o;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    x[2 * e] *= gelu_grad_f(bflo(pw[e]));
-                    x[2 * e + 1] *= gelu_grad_f(bfhi(pw[e]));
+                    x[2 * e] *= gelu_grad_f(bflo(pw[u][e]));
+                    x[2 * e + 1] *= gelu_grad_f(bfhi(pw[u][e]));
                     o[e] = pack_bf2(x[2 * e], x[2 * e + 1]);
                 }
-                *(u32x4*)(dst + r * (int64_t)N + cv * 8) = o;
+                *(u32x4*)(dst + (r + u) * (int64_t)N + cv * 8) = o;
                 // the bias gradient is the sum of the stored (bf16) dpre
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -110,24 +98,46 @@ __global__ __launch_bounds__(CS_THREADS) void colsum_kernel(const uint16_t* __re
                 }
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[q][e] += x[e];
+            for (int e = 0; e < 8; ++e) acc[e] += x[e];
         }
-    }
+    };
+    int64_t r = r0;
+    for (; r + CS_ROWS <= r1; r += CS_ROWS) rows_at(r, CS_ROWS);
+    if (r < r1) rows_at(r, (int)(r1 - r));
 #pragma unroll
-    for (int q = 0; q < CS_MAXV; ++q) {
-        const int cv = threadIdx.x + CS_THREADS * q;
-        if (cv >= nv) break;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) partial[(int64_t)blockIdx.x * N + cv * 8 + e] = acc[q][e];
-    }
+    for (int e = 0; e < 8; ++e) partial[(int64_t)blockIdx.x * N + cv * 8 + e] = acc[e];
 }
 
-__global__ void fold_colsum_kernel(const float* __restrict__ partial, int nblocks, int N, float* __restrict__ out) {
-    int c = blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= N) return;
+// out[c] += sum over the nblocks partial rows of column c.  A block takes 32
+// columns; its 32 phases of 32 threads each sum every 32nd partial row (phase ph:
+// rows ph, ph+32, ...), then the 32 phase sums are added in phase order.
+constexpr int FOLD_COLS = 32, FOLD_PHASES = 32;
+__global__ __launch_bounds__(FOLD_COLS * FOLD_PHASES) void fold_colsum_kernel(const float* __restrict__ partial,
+                                                                              int nblocks, int N,
+                                                                              float* __restrict__ out) {
+    __shared__ float red[FOLD_PHASES][FOLD_COLS];
+    const int cl = threadIdx.x % FOLD_COLS, ph = threadIdx.x / FOLD_COLS;
+    const int c = blockIdx.x * FOLD_COLS + cl;
     float s = 0.f;
-    for (int b = 0; b < nblocks; ++b) s += partial[(int64_t)b * N + c];
-    out[c] += s;
+    if (c < N) {
+        int b = ph;
+        for (; b + 3 * FOLD_PHASES < nblocks; b += 4 * FOLD_PHASES) {
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = partial[(int64_t)(b + u * FOLD_PHASES) * N + c];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s += v[u];
+        }
+        for (; b < nblocks; b += FOLD_PHASES) s += partial[(int64_t)b * N + c];
+    }
+    red[ph][cl] = s;
+    __syncthreads();
+    if (ph == 0 && c < N) {
+        float t = red[0][cl];
+#pragma unroll
+        for (int p = 1; p < FOLD_PHASES; ++p) t += red[p][cl];
+        out[c] += t;
+    }
 }
 
 // ---------------------------------------------------------------- cross-entropy
@@ -596,26 +606,26 @@ int64_t colsum_partial_elems(int64_t rows, int N) { return (int64_t)colsum_block
 hipError_t launch_bias_gelu_bwd(const uint16_t* pre, const uint16_t* dg, uint16_t* dpre, float* db, float* partial,
                                 int64_t rows, int N, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
-    if (N % 8 || N > 8 * CS_THREADS * CS_MAXV) return hipErrorInvalidValue;
+    if (N % 8 || N > 8 * CS_MAX_THREADS) return hipErrorInvalidValue;
     int blocks = colsum_blocks(rows);
-    PROF_LAUNCH(KC_GELU_BWD, 6.0 * rows * N, s, hipLaunchKernelGGL(colsum_kernel<true>, dim3(blocks), dim3(CS_THREADS), 0, s, dg, (int64_t)N, pre, dpre, partial,
+    PROF_LAUNCH(KC_GELU_BWD, 6.0 * rows * N, s, hipLaunchKernelGGL(colsum_kernel<true>, dim3(blocks), dim3(colsum_threads(N)), 0, s, dg, (int64_t)N, pre, dpre, partial,
                        rows, N));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    PROF_LAUNCH(KC_FOLD, 4.0 * blocks * N, s, hipLaunchKernelGGL(fold_colsum_kernel, dim3(cdiv(N, 256)), dim3(256), 0, s, partial, blocks, N, db));
+    PROF_LAUNCH(KC_FOLD, 4.0 * blocks * N, s, hipLaunchKernelGGL(fold_colsum_kernel, dim3(cdiv(N, FOLD_COLS)), dim3(FOLD_COLS * FOLD_PHASES), 0, s, partial, blocks, N, db));
     return hipGetLastError();
 }
 
 hipError_t launch_bias_grad(const uint16_t* dY, int64_t ldy, float* db, float* partial, int64_t rows, int N,
                             hipStream_t s) {
     if (rows <= 0) return hipSuccess;
-    if (N % 8 || N > 8 * CS_THREADS * CS_MAXV) return hipErrorInvalidValue;
+    if (N % 8 || N > 8 * CS_MAX_THREADS) return hipErrorInvalidValue;
     int blocks = colsum_blocks(rows);
-    PROF_LAUNCH(KC_COLSUM, 2.0 * rows * N, s, hipLaunchKernelGGL(colsum_kernel<false>, dim3(blocks), dim3(CS_THREADS), 0, s, dY, ldy, (const uint16_t*)nullptr,
+    PROF_LAUNCH(KC_COLSUM, 2.0 * rows * N, s, hipLaunchKernelGGL(colsum_kernel<false>, dim3(blocks), dim3(colsum_threads(N)), 0, s, dY, ldy, (const uint16_t*)nullptr,
                        (uint16_t*)nullptr, partial, rows, N));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fold_colsum_kernel, dim3(cdiv(N, 256)), dim3(256), 0, s, partial, blocks, N, db);
+    hipLaunchKernelGGL(fold_colsum_kernel, dim3(cdiv(N, FOLD_COLS)), dim3(FOLD_COLS * FOLD_PHASES), 0, s, partial, blocks, N, db);
     return hipGetLastError();
 }
 
