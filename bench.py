@@ -144,7 +144,7 @@ def main():
     torch.cuda.set_device(0)
     cfg = lib.make_config(L, H, C, V, Vp, Tmax, B, T)
     model = lib.GPT2(cfg, seed=1337)
-    nl = max(1, min(args.lanes, n_micro))
+    nl = max(1, min(args.lanes, n_micro, 1 + lib.MAX_LANES))
     lanes = [model] + [model.add_lane() for _ in range(nl - 1)]
     main_stream = torch.cuda.current_stream()
     streams = [torch.cuda.Stream() for _ in range(nl)] if nl > 1 else [main_stream]

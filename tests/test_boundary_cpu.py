@@ -118,6 +118,11 @@ def test_strerror(L):
         assert L.gpt2_strerror(s)
 
 
+def test_max_lanes_matches_header():
+    src = open(os.path.join(ROOT, "include", "gpt2mi.h")).read()
+    assert re.search(r"#define GPT2_MAX_LANES (\d+)", src).group(1) == str(lib.MAX_LANES)
+
+
 def test_lane_init_validates_without_a_device(L):
     # a lane needs a model handle and an output pointer
     lane = ctypes.c_void_p()

@@ -74,7 +74,8 @@ class Trainer:
         self.B, self.T, self.V, self.n_micro = B, T, V, n_micro
         self.cfg = lib.make_config(L, H, C, V, Vp, Tmax, B, T)
         self.model = lib.GPT2(self.cfg, seed=seed, init=init, device=device)
-        self.lanes = [self.model] + [self.model.add_lane() for _ in range(max(1, min(lanes, n_micro)) - 1)]
+        nl = max(1, min(lanes, n_micro, 1 + lib.MAX_LANES))
+        self.lanes = [self.model] + [self.model.add_lane() for _ in range(nl - 1)]
         self.data = synth.TokenStream(V, data_seed)
         self.step = 0  # completed optimizer steps
         self._setup(device)
