@@ -7,8 +7,9 @@ micro-steps per optimizer step; §4 optimisation: clip 1.0 + AdamW).
 A step = 9 x (gpt2_forward + gpt2_backward) + gpt2_clip_adamw at the
 warmup-step-350 learning rate, all on device-resident synthetic Zipf/EOT
 tokens.  Prints one JSON line (rank 0): tokens/s, MFU against the bf16 dense
-MFMA peak, the roofline of the dominant kernel (timed with HIP events on its
-stream during the timed region) and the CPU oracle timed on a bounded sample.
+MFMA peak, the roofline of the dominant kernel (HIP events recorded at each of
+its launches' start and end, on steps run right after the timed region) and the
+CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -263,7 +264,7 @@ def main():
                     "traffic_unit": "bytes per launch"}
         roof.update({"kernel": dominant, "launches": cnt, "avg_launch_ms": round(avg_ms, 4),
                      "work_per_launch": work / cnt,
-                     "timing": f"HIP events around every launch of the class on its stream, {n_roof} steps right "
+                     "timing": f"HIP events recorded by each launch of the class at the kernel's start and end, {n_roof} steps right "
                                "after the throughput region with the micro-steps in sequence",
                      "serial_ms_per_step": round(roof_wall * 1e3 / n_roof, 3)})
 

@@ -261,10 +261,12 @@ const char* gpt2_strerror(int status);
  * Kernel timing.  gpt2_prof_enable(h, kclass) starts recording: every launch
  * issued by this handle's gpt2_forward / gpt2_backward / gpt2_clip_adamw /
  * gpt2_eval_loss whose kernel class equals kclass (-1: every class; 0: stop)
- * is bracketed by a pair of HIP events on its stream, and the previous
+ * gets a pair of HIP events that the launch itself records at the kernel's
+ * own start and end (the six launches of the token-table gradient share one
+ * pair recorded on their stream before and after them), and the previous
  * records are dropped.  A class id names exactly one compiled kernel; its
  * name is gpt2_prof_class_name(kclass) (NULL for an unknown id), ids run
- * from 1 to 25.  gpt2_prof_read synchronises the stream and sums, over the
+ * from 1 to 26.  gpt2_prof_read synchronises the stream and sums, over the
  * recorded launches of class kclass (-1: all), the event-measured duration
  * (ms), the launch count and the algorithmic work (FLOP for the MFMA kernels
  * gemm_* and attn_fwd/dkdv/dq, bytes moved for the others).  At most 65,536

@@ -231,17 +231,30 @@ struct gpt2_handle {
     };
     struct Sink : ProfSink {
         gpt2_handle* h = nullptr;
-        bool active = false;
-        void begin(int cls, double work, hipStream_t s) override {
+        bool active = false, multi = false;
+        void begin(int cls, double work, hipStream_t s, bool many) override {
             active = false;
+            pend0 = pend1 = nullptr;
             if ((h->prof_class != -1 && h->prof_class != cls) || (int)h->recs.size() >= PROF_MAX) return;
             const size_t n = h->recs.size();
-            if (hipEventRecord(h->ev0[n], s) != hipSuccess) return;
+            multi = many;
+            if (multi) {
+                if (hipEventRecord(h->ev0[n], s) != hipSuccess) return;
+            } else {  // recorded by the launch itself at the kernel's start and end
+                pend0 = h->ev0[n];
+                pend1 = h->ev1[n];
+            }
             h->recs.push_back({cls, work});
             active = true;
         }
         void end(int, hipStream_t s) override {
-            if (active) (void)hipEventRecord(h->ev1[h->recs.size() - 1], s);  // a failed record only loses a timing
+            if (active) {
+                if (multi)
+                    (void)hipEventRecord(h->ev1[h->recs.size() - 1], s);  // a failed record only loses a timing
+                else if (pend0)
+                    h->recs.pop_back();  // nothing was launched
+            }
+            pend0 = pend1 = nullptr;
             active = false;
         }
     } sink;

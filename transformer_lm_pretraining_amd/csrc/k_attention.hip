@@ -598,7 +598,7 @@ hipError_t fwd_t(const uint16_t* qkv, uint16_t* out, float* lse, int B, int T, i
     const float sl = LOG2E / sqrtf((float)D);
     dim3 grid(attn_grid(B * H, T));
     PROF_LAUNCH(KC_ATTN_FWD, attn_work(B, T, H, D, 2), s,
-                hipLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(256), 0, s, qkv, out, lse, T, H, C, B * H, sl));
+                prof_launch(attn_fwd_kernel<D>, grid, dim3(256), 0, s, qkv, out, lse, T, H, C, B * H, sl));
     return hipGetLastError();
 }
 
@@ -609,12 +609,12 @@ hipError_t bwd_t(const uint16_t* qkv, const uint16_t* out, const uint16_t* dout,
     const float scale_log2 = LOG2E * scale;
     dim3 grid(attn_grid(B * H, T));
     PROF_LAUNCH(KC_ATTN_DQ, attn_work(B, T, H, D, 3), s,
-                hipLaunchKernelGGL(attn_dq_kernel<D>, grid, dim3(256), 0, s, qkv, out, dout, lse, dvec, dqkv, T, H, C,
+                prof_launch(attn_dq_kernel<D>, grid, dim3(256), 0, s, qkv, out, dout, lse, dvec, dqkv, T, H, C,
                                    B * H, scale_log2, scale));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     PROF_LAUNCH(KC_ATTN_DKDV, attn_work(B, T, H, D, 4), s,
-                hipLaunchKernelGGL(attn_dkdv_kernel<D>, grid, dim3(256), 0, s, qkv, dout, lse, dvec, dqkv, T, H, C,
+                prof_launch(attn_dkdv_kernel<D>, grid, dim3(256), 0, s, qkv, dout, lse, dvec, dqkv, T, H, C,
                                    B * H, scale_log2, scale));
     return hipGetLastError();
 }

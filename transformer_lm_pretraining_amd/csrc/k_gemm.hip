@@ -921,7 +921,7 @@ hipError_t run(GemmParams p, hipStream_t s) {
     dim3 grid(p.tiles_m * p.tiles_n * p.splits);
     const double work = 2.0 * p.M * p.N * (double)p.nk_total * BK;
     PROF_LAUNCH(gemm_class(A_T, EPI), work, s,
-                hipLaunchKernelGGL((gemm_kernel<BM, BN, WGM, WGN, A_T, B_T, EPI>), grid, dim3(64 * WGM * WGN), 0,
+                prof_launch((gemm_kernel<BM, BN, WGM, WGN, A_T, B_T, EPI>), grid, dim3(64 * WGM * WGN), 0,
                                    s, p));
     return hipGetLastError();
 }
@@ -940,11 +940,11 @@ hipError_t run_nt(GemmParams p, hipStream_t s) {
         const double work = 2.0 * p.M * p.N * (double)p.nk_total * BK;
         if (EPI == EPI_BF16 && p.res != nullptr)
             PROF_LAUNCH(gemm_class(false, EPI), work, s,
-                        hipLaunchKernelGGL((gemm_nt_w8_kernel<EPI_BF16R, NT_STAGES, NT_KD>), dim3(p.tiles_m * p.tiles_n),
+                        prof_launch((gemm_nt_w8_kernel<EPI_BF16R, NT_STAGES, NT_KD>), dim3(p.tiles_m * p.tiles_n),
                                            dim3(512), 0, s, p));
         else
             PROF_LAUNCH(gemm_class(false, EPI), work, s,
-                        hipLaunchKernelGGL((gemm_nt_w8_kernel<EPI, NT_STAGES, NT_KD>), dim3(p.tiles_m * p.tiles_n),
+                        prof_launch((gemm_nt_w8_kernel<EPI, NT_STAGES, NT_KD>), dim3(p.tiles_m * p.tiles_n),
                                            dim3(512), 0, s, p));
         return hipGetLastError();
     }
@@ -1062,7 +1062,7 @@ hipError_t run_tn_group(const TnJobDesc* jobs, int n, int M, float* partial, int
     if (sp == 1) {
         for (int j = 0; j < n; ++j) G.job[j].out = jobs[j].dW;
         PROF_LAUNCH(KC_GEMM_TN_ACC, work, s,
-                    hipLaunchKernelGGL((gemm_tn_w8_kernel<EPI_F32_ACC, TN_STAGES, TN_TD>), dim3(tiles), dim3(512),
+                    prof_launch((gemm_tn_w8_kernel<EPI_F32_ACC, TN_STAGES, TN_TD>), dim3(tiles), dim3(512),
                                        0, s, G));
         return hipGetLastError();
     }
@@ -1086,14 +1086,14 @@ hipError_t run_tn_group(const TnJobDesc* jobs, int n, int M, float* partial, int
         off += (int64_t)sp * jobs[j].N;
     }
     PROF_LAUNCH(KC_GEMM_TN_SPLIT, work, s,
-                hipLaunchKernelGGL((gemm_tn_w8_kernel<EPI_F32_STORE, TN_STAGES, TN_TD>), dim3(tiles * sp),
+                prof_launch((gemm_tn_w8_kernel<EPI_F32_STORE, TN_STAGES, TN_TD>), dim3(tiles * sp),
                                    dim3(512), 0, s, G));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n4 = std::max<int64_t>(R.start4[n], R.bstart[n]);
     const int blocks = (int)std::min<int64_t>(cdiv(n4, 256), 4096);
     PROF_LAUNCH(KC_SPLITK_REDUCE, 16.0 * n4 * (sp + 2), s,
-                hipLaunchKernelGGL(splitk_reduce_group_kernel, dim3(blocks), dim3(256), 0, s, R));
+                prof_launch(splitk_reduce_group_kernel, dim3(blocks), dim3(256), 0, s, R));
     return hipGetLastError();
 }
 

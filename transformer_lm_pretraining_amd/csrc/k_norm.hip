@@ -337,12 +337,12 @@ __global__ __launch_bounds__(256) void fold_finish_kernel(const float* __restric
 hipError_t fold_slots(float* partial, int64_t slot_elems, int nslots, int nblocks, int C, const LnFoldSet& set,
                       hipStream_t s) {
     PROF_LAUNCH(KC_FOLD, 8.0 * nblocks * C * nslots, s,
-                hipLaunchKernelGGL(fold_segments_kernel, dim3(cdiv(2 * C, 256), FOLD_SEGS, nslots), dim3(256), 0, s,
+                prof_launch(fold_segments_kernel, dim3(cdiv(2 * C, 256), FOLD_SEGS, nslots), dim3(256), 0, s,
                                    partial, slot_elems, nblocks, C));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     PROF_LAUNCH(KC_FOLD, 8.0 * std::min(FOLD_SEGS, nblocks) * C * nslots, s,
-                hipLaunchKernelGGL(fold_finish_kernel, dim3(cdiv(2 * C, 256), nslots), dim3(256), 0, s, partial,
+                prof_launch(fold_finish_kernel, dim3(cdiv(2 * C, 256), nslots), dim3(256), 0, s, partial,
                                    slot_elems, nblocks, C, set));
     return hipGetLastError();
 }
@@ -357,11 +357,11 @@ hipError_t ln_fwd_t(const uint16_t* x, const float* w, const float* b, uint16_t*
         // half-wave rows with 16-byte loads: eight rows per block of four waves
         const int blocks = (int)std::min<int64_t>(768, cdiv(rows, 2 * ROWS_PER_BLOCK));
         PROF_LAUNCH(KC_LN_FWD, 4.0 * rows * C, s,
-                    hipLaunchKernelGGL((ln_fwd16_kernel<C / 256>), dim3(blocks), dim3(256), 0, s, x, w, b, y, mean,
+                    prof_launch((ln_fwd16_kernel<C / 256>), dim3(blocks), dim3(256), 0, s, x, w, b, y, mean,
                                        rstd, rows));
     } else {
         PROF_LAUNCH(KC_LN_FWD, 4.0 * rows * C, s,
-                    hipLaunchKernelGGL((ln_fwd_kernel<VEC, NV>), dim3(ln_blocks(rows)), dim3(256), 0, s, x, w, b, y,
+                    prof_launch((ln_fwd_kernel<VEC, NV>), dim3(ln_blocks(rows)), dim3(256), 0, s, x, w, b, y,
                                        mean, rstd, rows));
     }
     return hipGetLastError();
@@ -374,7 +374,7 @@ hipError_t ln_bwd_t(const uint16_t* x, const uint16_t* dy, const float* w, const
                     hipStream_t s) {
     constexpr int C = NV * 64 * VEC;
     int blocks = ln_blocks(rows);
-    PROF_LAUNCH(KC_LN_BWD, 2.0 * rows * C * (accumulate ? 4 : 3), s, hipLaunchKernelGGL((ln_bwd_kernel<VEC, NV>), dim3(blocks), dim3(256), 0, s, x, dy, w, mean, rstd, dres_in, dres,
+    PROF_LAUNCH(KC_LN_BWD, 2.0 * rows * C * (accumulate ? 4 : 3), s, prof_launch((ln_bwd_kernel<VEC, NV>), dim3(blocks), dim3(256), 0, s, x, dy, w, mean, rstd, dres_in, dres,
                        accumulate, partial, rows));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || dw == nullptr) return e;  // no dw: the partials are folded later

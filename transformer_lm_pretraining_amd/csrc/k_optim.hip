@@ -256,15 +256,15 @@ hipError_t clip_adamw_ng(float* p, float* const* g, float* m, float* v, uint16_t
     const int64_t n4 = n / 4;
     GradSum<NG> G;
     for (int j = 0; j < NG; ++j) G.g[j] = (float4*)g[j];
-    PROF_LAUNCH(KC_SUMSQ, 4.0 * NG * n, s, hipLaunchKernelGGL(sumsq_kernel<NG>, dim3(NORM_BLOCKS), dim3(OPT_THREADS), 0, s, G, n4, partial));
+    PROF_LAUNCH(KC_SUMSQ, 4.0 * NG * n, s, prof_launch(sumsq_kernel<NG>, dim3(NORM_BLOCKS), dim3(OPT_THREADS), 0, s, G, n4, partial));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    PROF_LAUNCH(KC_NORM_FINAL, 8.0 * NORM_BLOCKS, s, hipLaunchKernelGGL(norm_finalize_kernel, dim3(1), dim3(OPT_THREADS), 0, s, partial, NORM_BLOCKS, a.max_norm,
+    PROF_LAUNCH(KC_NORM_FINAL, 8.0 * NORM_BLOCKS, s, prof_launch(norm_finalize_kernel, dim3(1), dim3(OPT_THREADS), 0, s, partial, NORM_BLOCKS, a.max_norm,
                        scale_dev, norm_dev));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     AdamwDev d{a.lr, a.beta1, a.beta2, a.eps, a.wd, a.inv_bc1, a.inv_bc2};
-    PROF_LAUNCH(KC_ADAMW, (24.0 + 8.0 * NG) * n + 2.0 * n_decay, s, hipLaunchKernelGGL(adamw_kernel<NG>, dim3(grid_for(n4, 8192)), dim3(OPT_THREADS), 0, s, (float4*)p, G,
+    PROF_LAUNCH(KC_ADAMW, (24.0 + 8.0 * NG) * n + 2.0 * n_decay, s, prof_launch(adamw_kernel<NG>, dim3(grid_for(n4, 8192)), dim3(OPT_THREADS), 0, s, (float4*)p, G,
                        (float4*)m, (float4*)v, (uint2*)shadow, n4, n_decay / 4, d, (const float*)scale_dev));
     return hipGetLastError();
 }
@@ -290,14 +290,14 @@ hipError_t launch_clip_adamw(float* p, float* g, float* m, float* v, uint16_t* s
 }
 
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {
-    PROF_LAUNCH(KC_OTHER, 6.0 * n, s, hipLaunchKernelGGL(cast_bf16_kernel, dim3(grid_for(n / 4)), dim3(OPT_THREADS), 0, s, (const float4*)src,
+    PROF_LAUNCH(KC_OTHER, 6.0 * n, s, prof_launch(cast_bf16_kernel, dim3(grid_for(n / 4)), dim3(OPT_THREADS), 0, s, (const float4*)src,
                        (uint2*)dst, n / 4));
     return hipGetLastError();
 }
 
 hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int R, int Cc, hipStream_t s) {
     dim3 grid((unsigned)cdiv(Cc, 64), (unsigned)cdiv(R, 64));
-    PROF_LAUNCH(KC_TRANSPOSE, 4.0 * R * Cc, s, hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, src, dst, R, Cc));
+    PROF_LAUNCH(KC_TRANSPOSE, 4.0 * R * Cc, s, prof_launch(transpose_bf16_kernel, grid, dim3(256), 0, s, src, dst, R, Cc));
     return hipGetLastError();
 }
 
@@ -331,7 +331,7 @@ hipError_t launch_transpose_bf16_batch(const uint16_t* const* src, uint16_t* con
         if (tiles == 0) continue;
         if (tiles > INT32_MAX) return hipErrorInvalidValue;
         PROF_LAUNCH(KC_TRANSPOSE, bytes, s,
-                    hipLaunchKernelGGL(transpose_batch_kernel, dim3((unsigned)tiles), dim3(256), 0, s, J));
+                    prof_launch(transpose_batch_kernel, dim3((unsigned)tiles), dim3(256), 0, s, J));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -340,14 +340,14 @@ hipError_t launch_transpose_bf16_batch(const uint16_t* const* src, uint16_t* con
 
 hipError_t launch_fill_f32(float* dst, float val, int64_t n, hipStream_t s) {
     if (n <= 0) return hipSuccess;
-    PROF_LAUNCH(KC_OTHER, 4.0 * n, s, hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_for(n)), dim3(256), 0, s, dst, val, n));
+    PROF_LAUNCH(KC_OTHER, 4.0 * n, s, prof_launch(fill_f32_kernel, dim3(grid_for(n)), dim3(256), 0, s, dst, val, n));
     return hipGetLastError();
 }
 
 hipError_t launch_init_normal(float* dst, int64_t n, uint64_t seed, int tensor, double stdv, int64_t zero_from,
                               hipStream_t s) {
     if (n <= 0) return hipSuccess;
-    PROF_LAUNCH(KC_OTHER, 4.0 * n, s, hipLaunchKernelGGL(init_normal_kernel, dim3(grid_for(n)), dim3(256), 0, s, dst, n, seed,
+    PROF_LAUNCH(KC_OTHER, 4.0 * n, s, prof_launch(init_normal_kernel, dim3(grid_for(n)), dim3(256), 0, s, dst, n, seed,
                        (uint64_t)tensor << 40, stdv, zero_from));
     return hipGetLastError();
 }

@@ -1,26 +1,70 @@
 // Optional per-launch kernel timing.  While a handle has timing enabled, the
-// C-ABI layer installs a thread-local sink; every launcher brackets its
-// hipLaunchKernelGGL with begin/end so one class id always names exactly one
-// compiled kernel (the ids are listed in include/gpt2mi.h).
+// C-ABI layer installs a thread-local sink; every launcher wraps its launch in
+// PROF_LAUNCH so one class id always names exactly one compiled kernel (the
+// ids are listed in include/gpt2mi.h).
+//
+// Inside PROF_LAUNCH a kernel goes out through prof_launch: when the sink has
+// selected the launch it hands over a start/stop event pair, and the launch
+// extension of the HIP runtime records them at that kernel's own start and
+// end, so the measured time excludes the host's dispatch and any gap in front
+// of the kernel on its stream.  PROF_SPAN times a group of launches with
+// events recorded on the stream before the first and after the last.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <cstdint>
+#include <tuple>
+#include <utility>
+
 struct ProfSink {
-    virtual void begin(int cls, double work, hipStream_t s) = 0;
+    // multi: the span holds several launches (stream-recorded events); else the
+    // sink may leave an event pair in pend0/pend1 for the span's prof_launch
+    virtual void begin(int cls, double work, hipStream_t s, bool multi) = 0;
     virtual void end(int cls, hipStream_t s) = 0;
     virtual ~ProfSink() {}
+    hipEvent_t pend0 = nullptr, pend1 = nullptr;
 };
 
 extern thread_local ProfSink* g_prof_sink;
 
-#define PROF_LAUNCH(cls, work, stream, ...)                                   \
+namespace prof_detail {
+template <class Tup, size_t... I>
+inline void arg_ptrs(Tup& t, void** out, std::index_sequence<I...>) {
+    ((out[I] = (void*)&std::get<I>(t)), ...);
+}
+}  // namespace prof_detail
+
+// Launches kernel(args...) on stream s; arguments are converted to the
+// kernel's parameter types as a triple-chevron launch would convert them.
+template <typename... Formal, typename... Actual>
+inline hipError_t prof_launch(void (*kernel)(Formal...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
+                              Actual&&... args) {
+    static_assert(sizeof...(Formal) == sizeof...(Actual), "kernel argument count");
+    std::tuple<Formal...> vals{static_cast<Formal>(std::forward<Actual>(args))...};
+    void* argv[sizeof...(Formal) + 1];
+    prof_detail::arg_ptrs(vals, argv, std::index_sequence_for<Formal...>{});
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (ProfSink* ps = g_prof_sink) {
+        e0 = ps->pend0;
+        e1 = ps->pend1;
+        ps->pend0 = ps->pend1 = nullptr;
+    }
+    if (e0) return hipExtLaunchKernel((const void*)kernel, grid, block, argv, shmem, s, e0, e1, 0);
+    return hipLaunchKernel((const void*)kernel, grid, block, argv, shmem, s);
+}
+
+#define PROF_TIMED_(multi, cls, work, stream, ...)                            \
     do {                                                                      \
         ProfSink* ps_ = g_prof_sink;                                          \
-        if (ps_) ps_->begin((cls), (work), (stream));                         \
+        if (ps_) ps_->begin((cls), (work), (stream), (multi));                \
         __VA_ARGS__;                                                          \
         if (ps_) ps_->end((cls), (stream));                                   \
     } while (0)
+
+#define PROF_LAUNCH(cls, work, stream, ...) PROF_TIMED_(false, cls, work, stream, __VA_ARGS__)
+#define PROF_SPAN(cls, work, stream, ...) PROF_TIMED_(true, cls, work, stream, __VA_ARGS__)
 
 // Kernel class ids (one compiled kernel each).
 enum KernelClass {
