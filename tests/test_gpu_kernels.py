@@ -178,7 +178,10 @@ def test_bias_grad_colsum(gpu_lib):
 
 # ---------------------------------------------------------------- GEMM
 
-@pytest.mark.parametrize("M,N,K", [(300, 200, 128), (256, 2304, 768), (1024, 50304, 768), (640, 768, 3072)])
+# (1024, 50304, 768), (2000, 9000, 64) and (3000, 6000, 128) run more 256x256 tiles than there
+# are CUs, with one-, two- and twelve-stage reductions and ragged last row / column tiles
+@pytest.mark.parametrize("M,N,K", [(300, 200, 128), (256, 2304, 768), (1024, 50304, 768), (640, 768, 3072),
+                                   (2000, 9000, 64), (3000, 6000, 128)])
 def test_gemm_nt_parity(gpu_lib, M, N, K):
     import torch
     from transformer_lm_pretraining_amd import lib
@@ -204,7 +207,8 @@ def test_gemm_nt_parity(gpu_lib, M, N, K):
     assert_elementwise(host(out), full, tol, "gemm_nt + bias + residual")
 
 
-@pytest.mark.parametrize("M", [333, 4000])  # small-shape kernel; 256x256-tile kernel with a ragged last row tile
+# small-shape kernel; 256x256-tile kernel with a ragged last row tile; 384 tiles (more than CUs)
+@pytest.mark.parametrize("M", [333, 4000, 8000])
 def test_gemm_nt_gelu_parity(gpu_lib, M):
     import torch
     from transformer_lm_pretraining_amd import lib
@@ -260,7 +264,7 @@ def test_gemm_tn_acc_parity(gpu_lib, M, N, K):
     assert rel_l2(host(dW2), ref) <= 1e-4
 
 
-@pytest.mark.parametrize("M", [515, 4000])
+@pytest.mark.parametrize("M", [515, 4000, 6900])  # 6900: 324 tiles (more than CUs), ragged last row tile
 def test_gemm_nt_dgelu_parity(gpu_lib, M):
     import torch
     from transformer_lm_pretraining_amd import lib

@@ -37,9 +37,10 @@ inline void arg_ptrs(Tup& t, void** out, std::index_sequence<I...>) {
 }  // namespace prof_detail
 
 // Launches kernel(args...) on stream s; arguments are converted to the
-// kernel's parameter types as a triple-chevron launch would convert them.
+// kernel's parameter types as a triple-chevron launch would convert them.  As
+// with that launch, a failure is read back with hipGetLastError.
 template <typename... Formal, typename... Actual>
-inline hipError_t prof_launch(void (*kernel)(Formal...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
+inline void prof_launch(void (*kernel)(Formal...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
                               Actual&&... args) {
     static_assert(sizeof...(Formal) == sizeof...(Actual), "kernel argument count");
     std::tuple<Formal...> vals{static_cast<Formal>(std::forward<Actual>(args))...};
@@ -51,8 +52,10 @@ inline hipError_t prof_launch(void (*kernel)(Formal...), dim3 grid, dim3 block, 
         e1 = ps->pend1;
         ps->pend0 = ps->pend1 = nullptr;
     }
-    if (e0) return hipExtLaunchKernel((const void*)kernel, grid, block, argv, shmem, s, e0, e1, 0);
-    return hipLaunchKernel((const void*)kernel, grid, block, argv, shmem, s);
+    if (e0)
+        (void)hipExtLaunchKernel((const void*)kernel, grid, block, argv, shmem, s, e0, e1, 0);
+    else
+        (void)hipLaunchKernel((const void*)kernel, grid, block, argv, shmem, s);
 }
 
 #define PROF_TIMED_(multi, cls, work, stream, ...)                            \
