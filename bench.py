@@ -107,8 +107,8 @@ def cpu_baseline(L, H, C, V, Vp, Tmax, T_sample, B_sample=3, n_adam=1 << 24, tok
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt2_124m", choices=sorted(WORKLOADS))
     ap.add_argument("--lanes", type=int, default=2,
                     help="micro-steps in flight at once, each lane on its own stream (1 = all on one stream)")
