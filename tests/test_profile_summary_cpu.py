@@ -58,3 +58,18 @@ def test_timeline_busy_overlap_and_active_time(tmp_path, capsys):
     assert gemm[-4:] == ["2", "90000.00", "180.00", "130.00"]
     ps.cmd_timeline(str(p), 0, 0, 10)
     assert ">= 2 kernels 0.0%" in capsys.readouterr().out
+
+
+def test_hbm_table_step_range_and_accumulators(tmp_path, capsys):
+    # step 1 of the synthetic trace: one LayerNorm forward of 10 ms (10,000 us)
+    p = tmp_path / "trace.csv"
+    write_trace(p, trace_rows())
+    ps.cmd_hbm(str(p), None, None, None, None, 12, 768, 19456, 1024, 50304, first=1, last=1)
+    ln = [l for l in capsys.readouterr().out.splitlines() if l.startswith("ln_fwd16")][0].split()
+    assert ln[-3:] == ["10000.00", "0.01", "0.001"]  # 59.9 MB in 10 ms
+    # algorithmic bytes of the update and the norm grow by 8 and 4 B per parameter with each accumulator
+    one = {k: b for k, _, b in ps.mem_kernels(12, 768, 19456, 1024, 50304, 1)}
+    two = {k: b for k, _, b in ps.mem_kernels(12, 768, 19456, 1024, 50304, 2)}
+    n_params = 124_475_904
+    assert two["adamw_kernel"] - one["adamw_kernel"] == 8 * n_params
+    assert two["sumsq_kernel"] == 2 * one["sumsq_kernel"] == 8 * n_params

@@ -283,21 +283,22 @@ def cmd_ntclass(path: str, L: int, C: int, BT: int, Vp: int, first=None, last=No
         flop / 1e9, flop / len(prods) / 1e9, flop / (t_micro * 1e-6) / 1e12, flop / (t_micro * 1e-6) / PEAK_BF16))
 
 
-def mem_kernels(L: int, C: int, BT: int, T: int, Vp: int):
-    """(kernel prefix, label, algorithmic bytes per launch)"""
+def mem_kernels(L: int, C: int, BT: int, T: int, Vp: int, G: int = 1):
+    """(kernel prefix, label, algorithmic bytes per launch); G gradient accumulators (one per lane)
+    are read by the norm and read and zeroed by the update"""
     n_decay = Vp * C + T * C + L * 12 * C * C
     n_params = n_decay + L * 13 * C + 2 * C
     return [("xent_kernel", "CE: logits read, dz written in place", 4 * BT * Vp),
             ("ln_fwd16_kernel", "LayerNorm fwd: R x, W y, W mean/rstd", 4 * BT * C + 8 * BT),
             ("ln_bwd_kernel", "LayerNorm bwd: R x, dy, dres, mean/rstd, W dx", 8 * BT * C + 8 * BT),
-            ("adamw_kernel", "AdamW: R p,g,m,v; W p,m,v; zero g; W shadow", 32 * n_params + 2 * n_decay),
-            ("sumsq_kernel", "global norm: R grads", 4 * n_params),
+            ("adamw_kernel", "AdamW: R p,g,m,v; W p,m,v; zero g; W shadow", (24 + 8 * G) * n_params + 2 * n_decay),
+            ("sumsq_kernel", "global norm: R grads", 4 * G * n_params),
             ("transpose_batch_kernel", "transposed bf16 weight copies, R + W", 4 * (Vp * C + 12 * L * C * C)),
             ("embedding_fwd_kernel", "embedding fwd: R wte rows, wpe rows, W x0", 4 * BT * C + 2 * T * C)]
 
 
-def cmd_hbm(path, fetch, write, cfetch, cwrite, L, C, BT, T, Vp) -> None:
-    d = by_grid(path)
+def cmd_hbm(path, fetch, write, cfetch, cwrite, L, C, BT, T, Vp, first=None, last=None, G=1) -> None:
+    d = by_grid(path, first, last)
     F = per_dispatch(fetch) if fetch else {}
     W = per_dispatch(write) if write else {}
     fs = (1 << 20) / copy_kib(cfetch, "FETCH_SIZE") if cfetch else None
@@ -305,7 +306,7 @@ def cmd_hbm(path, fetch, write, cfetch, cwrite, L, C, BT, T, Vp) -> None:
     if fs and ws:
         print("copy calibration: FETCH_SIZE x %.5f, WRITE_SIZE x %.5f" % (fs, ws))
     print("%-18s %-46s %9s %9s %6s %6s %10s" % ("kernel", "algorithmic bytes", "MB", "avg_us", "TB/s", "of 8", "counter MB"))
-    for pre, label, nbytes in mem_kernels(L, C, BT, T, Vp):
+    for pre, label, nbytes in mem_kernels(L, C, BT, T, Vp, G):
         ks = [k for k in d if k[0].startswith(pre)]
         if not ks:
             continue
@@ -326,6 +327,7 @@ def model_args(p) -> None:
     p.add_argument("--bt", type=int, default=19456)
     p.add_argument("--t", type=int, default=1024)
     p.add_argument("--vp", type=int, default=50304)
+    p.add_argument("--grads", type=int, default=1, help="gradient accumulators (lanes) the update reads")
 
 
 def main(argv=None):
@@ -358,6 +360,8 @@ def main(argv=None):
     model_args(n)
     h = sub.add_parser("hbm")
     h.add_argument("path")
+    h.add_argument("--first", type=int, help="first optimizer step of the trace to count (0-based)")
+    h.add_argument("--last", type=int, help="last optimizer step to count (inclusive)")
     for k in ("fetch", "write", "copy_fetch", "copy_write"):
         h.add_argument("--" + k.replace("_", "-"))
     model_args(h)
@@ -378,7 +382,8 @@ def main(argv=None):
         if a.fetch:
             nt_traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.layers, a.c, a.bt, a.vp)
     else:
-        cmd_hbm(a.path, a.fetch, a.write, a.copy_fetch, a.copy_write, a.layers, a.c, a.bt, a.t, a.vp)
+        cmd_hbm(a.path, a.fetch, a.write, a.copy_fetch, a.copy_write, a.layers, a.c, a.bt, a.t, a.vp, a.first,
+                a.last, a.grads)
 
 
 if __name__ == "__main__":
