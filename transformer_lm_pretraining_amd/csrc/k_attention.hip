@@ -327,8 +327,8 @@ __global__ __launch_bounds__(256, 2) void attn_dkdv_kernel(const uint16_t* __res
     auto load_block = [&](int i0) {
         stq.load(i0);
         sto.load(i0);
-        if (tid < KVB) {
-            rl = lse_bh[i0 + tid] * LOG2E;
+        if (tid < KVB) {  // consumed by store_block only, so the loads stay in flight through the block
+            rl = lse_bh[i0 + tid];
             rd = dv_bh[i0 + tid];
         }
     };
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256, 2) void attn_dkdv_kernel(const uint16_t* __res
         stq.store(sQ[buf], tid);
         sto.store(sdO[buf], tid);
         if (tid < KVB) {
-            sL[buf][tid] = rl;
+            sL[buf][tid] = rl * LOG2E;
             sDv[buf][tid] = rd;
         }
     };
