@@ -132,8 +132,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs the training step on one GPU only; multi-GPU runs "
-              "(--gpus > 1) are not part of it.", file=sys.stderr)
+        print("bench.py: the training step runs on one GPU only; --gpus > 1 (or WORLD_SIZE > 1) is not "
+              "supported.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
