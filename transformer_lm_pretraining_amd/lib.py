@@ -20,7 +20,8 @@ GPT2_OK, GPT2_E_INVALID, GPT2_E_SHAPE, GPT2_E_STATE, GPT2_E_HIP, GPT2_E_DATA, GP
 IGNORE_TARGET = -100  # GPT2_IGNORE_TARGET: a position whose loss is not taken
 MAX_LANES = 3         # GPT2_MAX_LANES: lanes per model (so at most four micro-steps in flight)
 # kernel classes whose work is counted in FLOP (the others count bytes)
-MFMA_CLASSES = ("gemm_nt", "gemm_nt_gelu", "gemm_tn_acc", "gemm_tn_splitk", "attn_fwd", "attn_dkdv", "attn_dq")
+MFMA_CLASSES = ("gemm_nt", "gemm_nt_gelu", "gemm_nt_dgelu", "gemm_tn_acc", "gemm_tn_splitk", "attn_fwd", "attn_dkdv",
+                "attn_dq")
 
 
 class Gpt2Error(RuntimeError):
