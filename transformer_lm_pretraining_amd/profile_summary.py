@@ -107,13 +107,15 @@ def cmd_counters(a, b, fetch, write, cfetch, cwrite, top: int) -> None:
 FWD_BLOCK = ["ln_fwd", "gemm_nt", "attn_fwd", "gemm_nt", "ln_fwd", "gemm_nt", "gemm_nt"]
 
 
-def cmd_block(path: str, layers: int) -> None:
-    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+def cmd_block(path: str, layers: int, first=None, last=None) -> None:
+    """Per-block time of a one-lane step trace (or of optimizer steps first..last of it)."""
+    rows = rows_in_steps(path, first, last)
     seq = [(short(r["Kernel_Name"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in rows]
     # micro-steps: each forward starts with the embedding kernel
     starts = [i for i, (n, _) in enumerate(seq) if n.startswith("embedding_fwd")]
+    whole = starts[1:-1] if first is None else starts  # a step range holds whole micro-steps
     blocks, dw = [], []
-    for s in starts[1:-1]:  # whole micro-steps only, the first one skipped (warm caches)
+    for s in whole:  # without a range the first one is skipped (warm caches)
         fwd = seq[s + 1: s + 1 + 7 * layers]
         assert all(n.startswith(p) for (n, _), p in zip(fwd, FWD_BLOCK * layers)), [n for n, _ in fwd[:7]]
         i = s + 1 + 7 * layers
@@ -343,6 +345,8 @@ def main(argv=None):
     bl = sub.add_parser("block")
     bl.add_argument("path")
     bl.add_argument("--layers", type=int, default=12)
+    bl.add_argument("--first", type=int, help="first optimizer step of the trace to count (0-based)")
+    bl.add_argument("--last", type=int, help="last optimizer step to count (inclusive)")
     tl = sub.add_parser("timeline")
     tl.add_argument("trace")
     tl.add_argument("--first", type=int, required=True, help="first optimizer step (0-based)")
@@ -371,7 +375,7 @@ def main(argv=None):
     elif a.cmd == "counters":
         cmd_counters(a.a, a.b, a.fetch, a.write, a.copy_fetch, a.copy_write, a.top)
     elif a.cmd == "block":
-        cmd_block(a.path, a.layers)
+        cmd_block(a.path, a.layers, a.first, a.last)
     elif a.cmd == "grid":
         cmd_grid(a.path, a.top)
     elif a.cmd == "timeline":
